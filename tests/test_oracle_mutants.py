@@ -1,0 +1,76 @@
+"""The oracle's pins must catch plausible mistakes.
+
+Each mutant is a copy of ``oracle/oracle.c`` with one mistake planted by text
+substitution (the committed oracle is never changed), compiled with gcc into a
+temporary directory.  The test requires that at least one check of
+``oracle_checks.ALL_CHECKS`` fails on every mutant.  No mutant reads or writes
+out of bounds, so they run in-process.
+"""
+
+import os
+
+import pytest
+
+import oracle
+import oracle_checks
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+MUTANTS = {
+    "xnor_sign_zero_negative": [("return (v < 0.0f) ? -1 : 1;", "return (v <= 0.0f) ? -1 : 1;")],
+    "and_sign_zero_negative": [("return (v < 0.0f) ? 0 : 1;", "return (v <= 0.0f) ? 0 : 1;")],
+    "msb_first_bit_order": [(">> (c % 32)", ">> (31 - c % 32)")],
+    "and_weights_pm1": [("if (type == ORACLE_AND) return bit;",
+                         "if (type == ORACLE_AND) return bit ? 1 : -1;")],
+    "xnor_weight_polarity": [("return bit ? 1 : -1;", "return bit ? -1 : 1;")],
+    "padding_clamps": [("if (ix < 0 || ix >= in_w) continue; /* padded tap: nothing */",
+                        "if (ix < 0 || ix >= in_w) ix = ix < 0 ? 0 : in_w - 1;")],
+    "padding_row_clamps": [("if (iy < 0 || iy >= in_h) continue; /* padded tap: nothing */",
+                            "if (iy < 0 || iy >= in_h) iy = iy < 0 ? 0 : in_h - 1;")],
+    "beta_divides_by_valid_taps": [
+        ("double sum = 0.0;\n                    for (int ky",
+         "double sum = 0.0; int cnt = 0;\n                    for (int ky"),
+        ("sum += am[((long)i * in_h + iy) * in_w + ix];",
+         "sum += am[((long)i * in_h + iy) * in_w + ix]; ++cnt;"),
+        ("b = sum / (double)(kernel_h * kernel_w);", "b = sum / (double)cnt;")],
+    "affine_offset_then_scale": [("v = fmaf(v, s, b);", "v = (v + b) * s;")],
+    "affine_two_roundings": [("v = fmaf(v, s, b);", "v = (float)(v * s) + b;")],
+    "a_map_over_word_width": [("am[p] = sum / (double)in_c;", "am[p] = sum / (double)(words * 32);")],
+    "a_map_before_affine": [("sum += fabs(xd[p * in_c + c]);", "sum += fabs((double)x[p * in_c + c]);")],
+    "ceil_mode_output_size": [("return (in + 2 * pad - k) / stride + 1;",
+                               "return (in + 2 * pad - k + stride - 1) / stride + 1;")],
+    "epilogue_drops_beta": [("double r = v * scale * bw[((long)i * out_h + oy) * out_w + ox] + bias;",
+                             "double r = v * scale + bias;")],
+    "relu_clamps_positive": [("if (neuron == ORACLE_NEURON_RELU && r < 0.0) r = 0.0;",
+                              "if (neuron == ORACLE_NEURON_RELU && r > 0.0) r = 0.0;")],
+    "missing_bias_is_one": [("(double)output_bias[co] : 0.0;", "(double)output_bias[co] : 1.0;")],
+    "scale_value_ignored": [("(double)output_scale[co] : (double)scale_value;",
+                             "(double)output_scale[co] : 1.0;")],
+    "flipped_kernel": [("weight_value(weight_bits, words, co, ky, kx, kernel_h, kernel_w, c, type)",
+                        "weight_value(weight_bits, words, co, kernel_h - 1 - ky, kernel_w - 1 - kx,"
+                        " kernel_h, kernel_w, c, type)")],
+    "stride_ignored_in_window": [
+        ("int iy = oy * stride_h - pad_h + ky;\n                        if (iy < 0 || iy >= in_h) continue; /* padded",
+         "int iy = oy - pad_h + ky;\n                        if (iy < 0 || iy >= in_h) continue; /* padded")],
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    src = open(SRC).read()
+    for old, new in MUTANTS[name]:
+        assert src.count(old) >= 1, f"mutation anchor not found: {old!r}"
+        src = src.replace(old, new, 1)
+    path = tmp_path / "mutant.c"
+    path.write_text(src)
+    so = str(tmp_path / f"libmutant_{name}.so")
+    oracle.build(str(path), so)
+    lib = oracle.load(so)
+    failed = []
+    for check in oracle_checks.ALL_CHECKS:
+        try:
+            check(lib)
+        except (AssertionError, ValueError):
+            failed.append(check.__name__)
+            break
+    assert failed, f"no pin catches mutant {name}"
