@@ -1,0 +1,182 @@
+#!/usr/bin/env python3
+"""Throughput of the binary-convolution forward pass on one MI355X.
+
+One step = one full forward call (pack + A map, beta, convolution with fused
+epilogue) over one batch of the measured layer, inputs already resident in
+HBM.  Prints one JSON line:
+  value      nominal bit-MACs (N*Ho*Wo*Cout*kh*kw*Cin) per second of whole
+             steps, in G bit-MAC/s (= binary GOPS);
+  roofline   the convolution kernel alone: its bit-MACs per launch over its
+             average duration (hipEvents recorded around that launch on the
+             launch stream), against the VALU popcount peak;
+  cpu_baseline  the CPU oracle timed on a bounded sample of the same layer.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layer I]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# 256 CUs x 64 lanes per clock x 2.4 GHz = 3.932e13 32-bit VALU lane-ops/s;
+# XNOR/AND cost 2 lane-ops (xor/and, then bcnt with accumulate) per 32 bit-MACs.
+VALU_LANE_OPS = 256 * 64 * 2.4e9
+POPCOUNT_PEAK_TBITMAC = VALU_LANE_OPS * 16 / 1e12          # 629.1
+# binaryWeights: one fp32 FMA per MAC on the VALU (packed forms not used).
+FP32_FMA_PEAK_TMAC = VALU_LANE_OPS / 1e12                  # 39.3
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--layer", type=int, default=None, help="index into workloads.LAYERS")
+    p.add_argument("--cpu-images", type=int, default=1,
+                   help="images of the layer the oracle runs for cpu_baseline (0: skip)")
+    p.add_argument("--cpu-repeats", type=int, default=3)
+    p.add_argument("--profile-only", action="store_true",
+                   help="run warmup + timed steps and print nothing else (for rocprofv3)")
+    return p.parse_args()
+
+
+def cpu_baseline(layer, inputs, images: int, repeats: int):
+    """Time the oracle (as it stands) on the first `images` images."""
+    import numpy as np
+
+    import oracle
+    sub = dict(inputs)
+    sub["x"] = np.ascontiguousarray(inputs["x"][:images])
+    threads = os.cpu_count() or 1
+    oracle.load()
+    best = None
+    for _ in range(max(1, repeats)):
+        t = time.perf_counter()
+        oracle.bconv_layer(layer, sub, threads=threads, want=("out",))
+        dt = time.perf_counter() - t
+        best = dt if best is None else min(best, dt)
+    macs = layer.nominal_macs(images)
+    return {"value": macs / best / 1e9, "unit": "GOPS (bit-MAC/s)" if layer.type != "binary_weights"
+            else "GMAC/s (fp32)", "cores": threads, "kind": "oracle",
+            "sample": f"{images} of {layer.n} images of {layer.name}, best of {repeats} runs "
+                      f"({best:.3f} s each, {macs} nominal MACs)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not offered (every box here has "
+              "one MI355X). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import popcount_convolution_amd as pca
+    from popcount_convolution_amd import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    index = workloads.LAYERS.index(workloads.BENCH_LAYER) if args.layer is None else args.layer
+    layer = workloads.LAYERS[index]
+    inputs = workloads.make_inputs(layer, workloads.layer_seed(index))
+    dev = torch.device("cuda:0")
+    conv = pca.BinaryConvolution.from_layer(layer, inputs)
+    n = layer.n
+    x = torch.from_numpy(inputs["x"]).to(dev)
+    out = torch.empty((n, conv.out_h, conv.out_w, conv.out_c), dtype=torch.float32, device=dev)
+    ws_bytes = max(1, conv.workspace_bytes(n))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+
+    # events around the convolution launch of every timed step
+    begins = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    for e in begins + ends:
+        e.record(stream)  # creates the underlying hipEvent
+    for _ in range(args.warmup):
+        pca.bconv_forward(conv.handle, sptr, n, x, out, ws, ws_bytes)
+    torch.cuda.synchronize()
+
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(args.steps):
+        pca.bconv_forward_profiled(conv.handle, sptr, n, x, out, ws, ws_bytes,
+                                   begins[i].cuda_event, ends[i].cuda_event)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    if args.profile_only:
+        return
+    total_ms = t0.elapsed_time(t1)
+    main_ms = float(np.mean([b.elapsed_time(e) for b, e in zip(begins, ends)]))
+    ms_per_step = total_ms / args.steps
+    macs = layer.nominal_macs()
+    value = macs / (ms_per_step / 1e3) / 1e9
+    binary = layer.type != "binary_weights"
+    achieved = macs / (main_ms / 1e3) / 1e12
+    peak = POPCOUNT_PEAK_TBITMAC if binary else FP32_FMA_PEAK_TMAC
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", "traffic.json")
+    kernel = conv.main_kernel(n)
+    if os.path.exists(tfile):
+        with open(tfile) as f:
+            t = json.load(f)
+        entry = t.get(layer.name)
+        if entry and entry.get("kernel") == kernel and entry.get("source_sha") == _kernel_sha():
+            traffic = entry.get("bytes_per_launch")
+    line = {
+        "metric": "binary conv GOPS (bit-MACs/s) and % of VALU popcount peak, 1 MI355X",
+        "value": round(value, 3),
+        "unit": "GOPS (bit-MAC/s)" if binary else "GMAC/s (fp32)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32" if binary else "f32",
+        "data": "synthetic (seeded; weight bits Bernoulli(0.5))",
+        "config": {"workload": layer.name, "type": layer.type, "batch": n,
+                   "input_hwc": [layer.in_h, layer.in_w, layer.in_c], "out_c": layer.out_c,
+                   "kernel": [layer.kernel_h, layer.kernel_w],
+                   "stride": [layer.stride_h, layer.stride_w], "pad": [layer.pad_h, layer.pad_w],
+                   "beta": layer.use_beta, "input_affine": layer.iscale_dist is not None,
+                   "neuron": layer.neuron, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "alu", "kernel": kernel, "achieved": round(achieved, 3),
+                     "peak": round(peak, 3),
+                     "unit": "Tbit-MAC/s" if binary else "TMAC/s (fp32 FMA)",
+                     "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "avg_kernel_us": round(main_ms * 1e3, 3)},
+    }
+    if args.cpu_images > 0:
+        line["cpu_baseline"] = cpu_baseline(layer, inputs, min(args.cpu_images, n), args.cpu_repeats)
+    else:
+        line["cpu_baseline"] = None
+    conv.close()
+    print(json.dumps(line), flush=True)
+
+
+def _kernel_sha() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "popcount_convolution_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,209 @@
+/*
+ * bconv.h -- binary convolution on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libbconv.so.  The operation is the one defined on Apple's
+ * "MPSCNNBinaryConvolution" documentation page (Overview, output equation):
+ *
+ *   out[i,y,x,c] = neuron( (sum over the window taps (ky,kx) and the input
+ *                  channels f of  in'[i,y',x',f] (*) B[c,ky,kx,f])
+ *                  * scale[c] * beta[i,y,x] + bias[c] )
+ *
+ * where (*) is one of the three forms of the page's type bullets:
+ *   BCONV_BINARY_WEIGHTS  full-precision input times the weight read as +-1;
+ *   BCONV_XNOR            input binarised by its sign, XNOR product read as
+ *                         +-1 (a 32-bit word pair gives 32 - 2*popcount(x^w));
+ *   BCONV_AND             input binarised, AND product read as 0/1 (a word
+ *                         pair gives popcount(x & w)).
+ * in' is the input after the optional per-channel input scale and bias (the
+ * page's input-terms paragraph), beta is the optional box average of the
+ * per-pixel mean |in'| (the page's two beta equations), and the fully
+ * connected layer of Apple's "MPSCNNFullyConnected" page (Overview,
+ * conditions) is the case kernel = source size, stride 1, no padding.
+ *
+ * Conventions fixed by this library where the pages are silent:
+ *   - Tensors are fp32, NHWC, dense: input [n][in_h][in_w][in_c], output
+ *     [n][out_h][out_w][out_c].  x indexes width, y height.
+ *   - Weight bits are uint32 words [out_c][kernel_h][kernel_w][ceil(in_c/32)];
+ *     input channel f is bit (f % 32) of word (f / 32).  Bit 1 is +1 (XNOR,
+ *     binaryWeights) or 1 (AND); bit 0 is -1 or 0.  Bits at positions >= in_c
+ *     in the last word are ignored.
+ *   - Geometry: out_h = (in_h + 2*pad_h - kernel_h)/stride_h + 1 (likewise w);
+ *     tap ky of output y reads input row y*stride_h - pad_h + ky.  With an odd
+ *     kernel, pad = kernel/2 and stride 1 this is the page's centred window
+ *     [-k/2, (k-1)/2].  Taps outside the image contribute nothing.
+ *   - in' = fmaf(in, input_scale[f], input_bias[f]) in fp32; the sign is
+ *     taken as (in' < 0) ? -1 : +1 (so -0 and NaN binarise to +1);
+ *     subnormals are kept.
+ *   - beta[i,y,x] = (sum of A over the window's in-image taps)/(kernel_h *
+ *     kernel_w), A[i,y,x] = sum_f |in'[i,y,x,f]| / in_c; beta = 1 without
+ *     BCONV_FLAG_USE_BETA_SCALING.  It applies to all three forms.
+ *   - A missing output scale array means the scalar desc.scale_value; missing
+ *     biases mean 0; a missing input scale means 1.
+ *   - neuron: none, or ReLU  r < 0 ? 0 : r.
+ *
+ * Results: XNOR/AND window sums are exact integers; the fp32 epilogue and
+ * the binaryWeights fp32 accumulation agree with an exact evaluation to a
+ * normwise relative 1e-5.
+ *
+ * Errors: every call returns a bconv_status_t; argument errors are detected
+ * on the host before anything is launched.  HIP failures return
+ * BCONV_ERR_HIP; bconv_last_error() gives the text (per calling thread).
+ */
+#ifndef BCONV_H
+#define BCONV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct bconv_handle *bconv_t;
+
+typedef enum {
+    BCONV_OK = 0,
+    BCONV_ERR_INVALID_ARGUMENT = 1, /* a size, pointer or enum out of range */
+    BCONV_ERR_UNSUPPORTED = 2,      /* defined by the pages but not offered (groups > 1) */
+    BCONV_ERR_WORKSPACE = 3,        /* workspace missing or smaller than required */
+    BCONV_ERR_ALLOC = 4,            /* device or host allocation failed at create */
+    BCONV_ERR_HIP = 5               /* a HIP runtime call failed; see bconv_last_error() */
+} bconv_status_t;
+
+/* The three operator forms (MPSCNNBinaryConvolution, Overview, type bullets). */
+typedef enum {
+    BCONV_BINARY_WEIGHTS = 0,
+    BCONV_XNOR = 1,
+    BCONV_AND = 2
+} bconv_type_t;
+
+/* Flags (MPSCNNBinaryConvolution, Overview, beta paragraph: beta is not an
+ * input; a flag turns it on). */
+enum {
+    BCONV_FLAG_NONE = 0u,
+    BCONV_FLAG_USE_BETA_SCALING = 1u
+};
+
+/* The activation applied last (MPSCNNBinaryConvolution, Overview, closing
+ * sentence of the description). */
+typedef enum {
+    BCONV_NEURON_NONE = 0,
+    BCONV_NEURON_RELU = 1
+} bconv_neuron_t;
+
+/* Layer shape (the convolution descriptor of the pages: kernel width/height,
+ * strides, groups).  The batch size is given per call. */
+typedef struct {
+    int32_t in_h, in_w, in_c; /* source image height, width, feature channels (>= 1) */
+    int32_t out_c;            /* output feature channels (>= 1) */
+    int32_t kernel_h, kernel_w; /* >= 1; kernel_h <= in_h + 2*pad_h, likewise w */
+    int32_t stride_h, stride_w; /* >= 1 */
+    int32_t pad_h, pad_w;     /* leading = trailing zero padding, 0 <= pad < kernel */
+    int32_t groups;           /* must be 1 (MPSCNNBinaryConvolution, groups note) */
+    int32_t neuron;           /* bconv_neuron_t */
+    float scale_value;        /* output scale used when output_scale is NULL */
+} bconv_desc_t;
+
+/* Where the per-step intermediates sit in a forward call's workspace, for
+ * checking each step on its own.  Offsets are in bytes from the workspace
+ * start; SIZE_MAX marks a section the handle does not use.
+ *   bits: uint32 [n][bits_rows][bits_cols][bits_words], the binarised input
+ *         with a zero halo of bits_pad_h rows and bits_pad_w columns on each
+ *         side; channel f of pixel (y,x) is bit (f%32) of word f/32 at
+ *         row y + bits_pad_h, column x + bits_pad_w.
+ *   a_map: float [n][in_h][in_w];  beta: float [n][out_h][out_w]. */
+typedef struct {
+    size_t bits_offset;
+    int32_t bits_rows, bits_cols, bits_words, bits_pad_h, bits_pad_w;
+    size_t a_map_offset;
+    size_t beta_offset;
+    size_t total_bytes;
+} bconv_workspace_layout_t;
+
+/* Checks a descriptor, form and flags without touching any device.
+ * INVALID_ARGUMENT for out-of-range values, UNSUPPORTED for groups != 1.
+ * Also enforces in_c*kernel_h*kernel_w <= 2^24 so every window sum is exact
+ * in int32 and in fp32. */
+bconv_status_t bconv_validate_desc(const bconv_desc_t *desc, int32_t type, uint32_t flags);
+
+/* Builds a layer on the current HIP device (MPSCNNBinaryConvolution, Topics,
+ * the initializer taking convolution data, output bias/scale, input
+ * bias/scale, type and flags; the scaleValue initializer is output_scale =
+ * NULL with desc.scale_value).
+ *   weight_bits   host, uint32 [out_c][kernel_h][kernel_w][ceil(in_c/32)]
+ *   output_scale  host, float [out_c] or NULL (-> desc.scale_value)
+ *   output_bias   host, float [out_c] or NULL (-> 0)
+ *   input_scale   host, float [in_c]  or NULL (-> 1)
+ *   input_bias    host, float [in_c]  or NULL (-> 0)
+ * Every array is copied; the caller keeps ownership of its buffers.  The
+ * weights are rearranged on the device into the layouts the kernels read.
+ * Synchronous.  On success *out receives a handle to release with
+ * bconv_destroy. */
+bconv_status_t bconv_create(const bconv_desc_t *desc, const uint32_t *weight_bits,
+                            const float *output_scale, const float *output_bias,
+                            const float *input_scale, const float *input_bias, int32_t type,
+                            uint32_t flags, bconv_t *out);
+
+/* The fully connected layer (MPSCNNFullyConnected, Overview and conditions):
+ * bconv_create with kernel = source size, stride 1, pad 0, groups 1; the
+ * output is [n][1][1][out_c] = [n][out_c].  The weight words are
+ * [out_c][in_h][in_w][ceil(in_c/32)], i.e. a row per output over the NHWC
+ * flattening of the source (the page's matrix view). */
+bconv_status_t bconv_create_fc(int32_t in_h, int32_t in_w, int32_t in_c, int32_t out_c,
+                               int32_t neuron, float scale_value, const uint32_t *weight_bits,
+                               const float *output_scale, const float *output_bias,
+                               const float *input_scale, const float *input_bias, int32_t type,
+                               uint32_t flags, bconv_t *out);
+
+/* Channel counts and output extent (MPSCNNBinaryConvolution, Topics,
+ * inputFeatureChannels / outputFeatureChannels).  Any pointer may be NULL. */
+bconv_status_t bconv_get_info(bconv_t h, int32_t *in_c, int32_t *out_c, int32_t *out_h,
+                              int32_t *out_w);
+
+/* Workspace bytes a forward call with batch n needs (0 is possible). */
+bconv_status_t bconv_workspace_size(bconv_t h, int32_t n, size_t *bytes);
+
+/* Layout of the workspace for batch n (see bconv_workspace_layout_t). */
+bconv_status_t bconv_workspace_layout(bconv_t h, int32_t n, bconv_workspace_layout_t *layout);
+
+/* Forward pass, asynchronous on `stream` (a hipStream_t; NULL = default
+ * stream).  `in`, `out` and `workspace` are device pointers owned by the
+ * caller and must stay valid until the stream work completes; `in` and `out`
+ * must not overlap.  n == 0 is a no-op.  Never allocates and never
+ * synchronises.  One handle may serve several streams at once when each call
+ * has its own workspace. */
+bconv_status_t bconv_forward(bconv_t h, void *stream, int32_t n, const float *in, float *out,
+                             void *workspace, size_t workspace_bytes);
+
+/* As bconv_forward, but writes the window sums instead of the epilogue:
+ * int32 for XNOR (the +-1 sum over in-image taps) and AND (the 0/1 sum);
+ * float for binaryWeights.  Same shape as the output. */
+bconv_status_t bconv_forward_accum(bconv_t h, void *stream, int32_t n, const float *in,
+                                   void *acc, void *workspace, size_t workspace_bytes);
+
+/* As bconv_forward, and records the hipEvent_t `main_begin` / `main_end`
+ * (either may be NULL) on `stream` immediately before and after the launch of
+ * the convolution / matrix kernel, so a caller can time that kernel alone. */
+bconv_status_t bconv_forward_profiled(bconv_t h, void *stream, int32_t n, const float *in,
+                                      float *out, void *workspace, size_t workspace_bytes,
+                                      void *main_begin, void *main_end);
+
+/* Name of the kernel bconv_forward_profiled brackets for batch n (a static
+ * string; "" for an invalid handle). */
+const char *bconv_main_kernel(bconv_t h, int32_t n);
+
+/* Releases the handle's device memory.  The caller must make sure no queued
+ * forward call still uses it.  NULL is accepted. */
+bconv_status_t bconv_destroy(bconv_t h);
+
+/* Static text of a status code. */
+const char *bconv_status_string(bconv_status_t s);
+
+/* Text of the last error raised on the calling thread ("" if none). */
+const char *bconv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BCONV_H */

@@ -1,0 +1,71 @@
+// Internal declarations shared by the host library and the kernel files of
+// libbconv.so.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "bconv.h"
+
+namespace bconv {
+
+// Output channels handled by one wave in the lane-per-channel kernels.
+constexpr int kTile = 64;
+
+// Geometry of one forward call, resolved on the host.
+struct Geom {
+    int n, in_h, in_w, in_c, out_c;
+    int kh, kw, sh, sw, ph, pw;
+    int out_h, out_w;
+    int words;        // ceil(in_c / 32)
+    int tiles;        // ceil(out_c / kTile)
+    // binarised-input buffer with a zero halo
+    int bits_rows;    // in_h + 2*ph
+    int bits_cols;    // in_w + 2*pw
+    int bits_halo_h, bits_halo_w;
+    long long bits_slack_words;  // zero words after the last image (strip over-reads)
+};
+
+// Per-lane weight words, grouped by kernel row: [tiles][kh][kwc4][64][4],
+// kwc4 = ceil(kw*words / 4).  Within row ky, word r = kx*words + w; lane l
+// of tile t holds output channel t*64 + l, so a wave reads 256 contiguous
+// bytes per 4 words.  Channels >= out_c and words past kw*words are zero; bits
+// >= in_c are cleared.
+struct LaneWeights {
+    const uint32_t *words;  // device
+    const int32_t *rect;    // [tiles][(kh+1)*(kw+1)][64]: prefix sums of tap popcounts
+    int kwc4;
+};
+
+// Epilogue operands.
+struct Epilogue {
+    const float *scale;  // [out_c] or nullptr -> scale_value
+    const float *bias;   // [out_c] or nullptr -> 0
+    float scale_value;
+    const float *beta;   // [n][out_h][out_w] or nullptr -> 1
+    int relu;
+};
+
+// Launchers (each returns the hipGetLastError() of its launch).
+hipError_t launch_pack(const Geom &g, hipStream_t s, const float *x, const float *in_scale,
+                       const float *in_bias, uint32_t *bits, float *a_map);
+hipError_t launch_beta(const Geom &g, hipStream_t s, const float *a_map, float *beta);
+hipError_t launch_prepack(const Geom &g, hipStream_t s, const uint32_t *user_bits, uint32_t *lane_words,
+                          int32_t *lane_popc, float *pm_weights, int pm_cols, int type);
+// Returns true when a specialised convolution kernel exists for this shape.
+bool xconv_fast_available(const Geom &g);
+// Output pixels per strip of the specialised kernel (sizes the over-read slack).
+int xconv_strip_width(const Geom &g);
+const char *xconv_kernel_name(const Geom &g);
+hipError_t launch_xconv(const Geom &g, hipStream_t s, int and_mode, const uint32_t *bits,
+                        const LaneWeights &w, const Epilogue &e, float *out, int32_t *acc_out,
+                        bool allow_fast);
+// Columns of the +-1.0f binaryWeights table (out_c rounded up to the channel block).
+int bwconv_pm_cols(int out_c);
+const char *bwconv_kernel_name(const Geom &g);
+hipError_t launch_bwconv(const Geom &g, hipStream_t s, const float *x, const float *in_scale,
+                         const float *in_bias, const float *pm_weights, int pm_cols,
+                         const Epilogue &e, float *out, float *acc_out);
+
+}  // namespace bconv

@@ -1,0 +1,320 @@
+// XNOR / AND binary convolution: the window sum of Apple
+// "MPSCNNBinaryConvolution" (Overview, output equation) with the XNOR and AND
+// products of its type bullets, one 32-bit word pair at a time:
+//   XNOR: 32 - 2*popcount(x ^ w) per word, so a window sums to
+//         Cin*taps_in_image - 2*popcount-sum of the disagreements;
+//   AND:  popcount(x & w) per word.
+// followed by the fused epilogue  neuron(v*scale[c]*beta + bias[c]).
+//
+// Mapping on gfx950: a wave owns 64 output channels (one per lane).  Each
+// lane keeps its channel's whole weight window in VGPRs.  The binarised
+// input words of a strip of P neighbouring output pixels are the same for
+// every lane, so they are fetched with scalar loads into SGPRs and fed to
+// v_xor_b32 / v_and_b32 as the scalar operand; v_bcnt_u32_b32 then counts and
+// accumulates in one instruction.  Two VALU instructions per word pair, no LDS
+// and no vector loads in the inner loop.
+#include "internal.h"
+
+namespace bconv {
+namespace {
+
+typedef const uint32_t __attribute__((address_space(4))) *scalar_u32_ptr;
+typedef const float __attribute__((address_space(4))) *scalar_f32_ptr;
+
+struct XArgs {
+    const uint32_t *bits;   // padded binarised input
+    const uint32_t *wlane;  // [tiles][kh][kwc4][64][4]
+    const int32_t *wrect;   // [tiles][(kh+1)*(kw+1)][64]
+    const float *scale, *bias, *beta;
+    float scale_value;
+    int relu;
+    float *out;
+    int32_t *acc_out;
+    int n, in_h, in_w, in_c, out_c, out_h, out_w;
+    int kh, kw, sh, sw, ph, pw, words;
+    int rows, cols;  // padded extent (halo = pad)
+    int kwc4, tiles;
+    int strips_per_row;
+    long long strips;
+};
+
+__device__ __forceinline__ void store_result(const XArgs &a, long long pix, int co, int v,
+                                             float sc, float bi, float be)
+{
+    if (co >= a.out_c) return;
+    const long long o = pix * a.out_c + co;
+    if (a.acc_out) {
+        a.acc_out[o] = v;
+        return;
+    }
+    float r = __builtin_fmaf((float)v * sc, be, bi);
+    if (a.relu) r = (r < 0.0f) ? 0.0f : r;
+    a.out[o] = r;
+}
+
+// Specialised kernel: kernel KHxKW, CW words per pixel, horizontal stride SW,
+// P output pixels per strip.  One wave = one (strip, 64-channel tile).
+template <int KH, int KW, int CW, int SW, int P, bool AND>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void xconv_fast(XArgs a)
+{
+    constexpr int RW = KW * CW;            // weight words per kernel row
+    constexpr int RW4 = (RW + 3) / 4;
+    constexpr int CWC = CW < 4 ? CW : 4;  // words per scalar-load chunk
+    constexpr int NCH = CW / CWC;
+    constexpr int NCOL = (P - 1) * SW + KW;
+    static_assert(CW % CWC == 0, "word chunking");
+
+    // Work indices fit 31 bits (the host checks strips * tiles < 2^31).
+    const int lane = threadIdx.x & 63;
+    const unsigned gw = blockIdx.x * 4u + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const unsigned tile = gw % (unsigned)a.tiles;
+    const unsigned strip = gw / (unsigned)a.tiles;
+    if (strip >= (unsigned)a.strips) return;
+
+    const unsigned row = strip / (unsigned)a.strips_per_row;
+    const int ow0 = (int)(strip % (unsigned)a.strips_per_row) * P;
+    const int img = (int)(row / (unsigned)a.out_h);
+    const int oy = (int)(row % (unsigned)a.out_h);
+
+    uint32_t acc[P];
+#pragma unroll
+    for (int p = 0; p < P; ++p) acc[p] = 0;
+
+    const scalar_u32_ptr bits = (scalar_u32_ptr)a.bits;
+    const uint4 *wl = reinterpret_cast<const uint4 *>(a.wlane) + (long long)tile * KH * RW4 * 64 + lane;
+    // Kernel rows stay a rolled loop: the strip words are invariant loads, and
+    // an unrolled row loop lets the compiler hoist every row's scalar loads
+    // at once, which overflows the SGPR file.  The row's weights (RW words)
+    // are re-read from the L1/L2-resident table each row.
+#pragma unroll 1
+    for (int ky = 0; ky < KH; ++ky) {
+        uint32_t w[RW4 * 4];
+#pragma unroll
+        for (int q = 0; q < RW4; ++q) {
+            const uint4 v = wl[(ky * RW4 + q) * 64];
+            w[4 * q + 0] = v.x;
+            w[4 * q + 1] = v.y;
+            w[4 * q + 2] = v.z;
+            w[4 * q + 3] = v.w;
+        }
+        const long long base = (((long long)img * a.rows + oy * a.sh + ky) * a.cols + (long long)ow0 * SW) * CW;
+#pragma unroll
+        for (int ch = 0; ch < NCH; ++ch) {
+            uint32_t x[NCOL * CWC];
+#pragma unroll
+            for (int col = 0; col < NCOL; ++col)
+#pragma unroll
+                for (int j = 0; j < CWC; ++j) x[col * CWC + j] = bits[base + col * CW + ch * CWC + j];
+#pragma unroll
+            for (int p = 0; p < P; ++p)
+#pragma unroll
+                for (int kx = 0; kx < KW; ++kx)
+#pragma unroll
+                    for (int j = 0; j < CWC; ++j) {
+                        const uint32_t xv = x[(p * SW + kx) * CWC + j];
+                        const uint32_t wv = w[kx * CW + ch * CWC + j];
+                        acc[p] += __builtin_popcount(AND ? (xv & wv) : (xv ^ wv));
+                    }
+        }
+    }
+
+    const int co = tile * kTile + lane;
+    const bool co_ok = co < a.out_c;
+    const float sc = a.scale ? (co_ok ? a.scale[co] : 0.0f) : a.scale_value;
+    const float bi = a.bias ? (co_ok ? a.bias[co] : 0.0f) : 0.0f;
+    const scalar_f32_ptr beta = (scalar_f32_ptr)a.beta;
+    // In-image tap rectangle [r0, r1) x [c0, c1) of each output pixel.  Every
+    // window holds at least one in-image tap because pad < kernel.
+    const int iy0 = oy * a.sh - a.ph;
+    const int r0 = iy0 < 0 ? -iy0 : 0;
+    const int r1 = a.in_h - iy0 < KH ? a.in_h - iy0 : KH;
+    const int32_t *rect = a.wrect + (long long)tile * (KH + 1) * (KW + 1) * 64 + lane;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        const int ox = ow0 + p;
+        if (ox >= a.out_w) break;
+        const long long pix = ((long long)img * a.out_h + oy) * a.out_w + ox;
+        int v;
+        if (AND) {
+            v = (int)acc[p];  // a zero word at a padded tap adds nothing
+        } else {
+            const int ix0 = ox * SW - a.pw;
+            const int c0 = ix0 < 0 ? -ix0 : 0;
+            const int c1 = a.in_w - ix0 < KW ? a.in_w - ix0 : KW;
+            const int valid = (r1 - r0) * (c1 - c0);
+            int corr = 0;
+            if (valid != KH * KW) {
+                // set weight bits at padded taps = total - in-image rectangle
+                const int total = rect[(KH * (KW + 1) + KW) * 64];
+                const int inside = rect[(r1 * (KW + 1) + c1) * 64] - rect[(r0 * (KW + 1) + c1) * 64] -
+                                   rect[(r1 * (KW + 1) + c0) * 64] + rect[(r0 * (KW + 1) + c0) * 64];
+                corr = total - inside;
+            }
+            v = a.in_c * valid - 2 * ((int)acc[p] - corr);
+        }
+        const float be = a.beta ? beta[pix] : 1.0f;
+        store_result(a, pix, co, v, sc, bi, be);
+    }
+}
+
+// Any geometry: one wave = one output pixel and a 64-channel tile; taps
+// outside the image are skipped, so no correction is needed.
+__global__ __launch_bounds__(256) void xconv_generic(XArgs a, int and_mode)
+{
+    // Work indices fit 31 bits (the host checks pixels * tiles < 2^31).
+    const int lane = threadIdx.x & 63;
+    const unsigned gw = blockIdx.x * 4u + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const unsigned tile = gw % (unsigned)a.tiles;
+    const unsigned upix = gw / (unsigned)a.tiles;
+    if (upix >= (unsigned)a.n * (unsigned)a.out_h * (unsigned)a.out_w) return;
+    const long long pix = upix;
+    const int ox = (int)(upix % (unsigned)a.out_w);
+    const int oy = (int)((upix / (unsigned)a.out_w) % (unsigned)a.out_h);
+    const int img = (int)(upix / ((unsigned)a.out_w * (unsigned)a.out_h));
+    const scalar_u32_ptr bits = (scalar_u32_ptr)a.bits;
+    const uint32_t *wl = a.wlane + (long long)tile * a.kh * a.kwc4 * 256 + lane * 4;
+    uint32_t acc = 0;
+    int valid = 0;
+    for (int ky = 0; ky < a.kh; ++ky) {
+        const int iy = oy * a.sh - a.ph + ky;
+        if (iy < 0 || iy >= a.in_h) continue;
+        for (int kx = 0; kx < a.kw; ++kx) {
+            const int ix = ox * a.sw - a.pw + kx;
+            if (ix < 0 || ix >= a.in_w) continue;
+            ++valid;
+            const long long base =
+                (((long long)img * a.rows + iy + a.ph) * a.cols + ix + a.pw) * a.words;
+            const int r0 = kx * a.words;
+            for (int j = 0; j < a.words; ++j) {
+                const int r = r0 + j;
+                const uint32_t xv = bits[base + j];
+                const uint32_t wv = wl[(ky * a.kwc4 + (r >> 2)) * 256 + (r & 3)];
+                acc += __builtin_popcount(and_mode ? (xv & wv) : (xv ^ wv));
+            }
+        }
+    }
+    const int co = tile * kTile + lane;
+    const bool co_ok = co < a.out_c;
+    const int v = and_mode ? (int)acc : a.in_c * valid - 2 * (int)acc;
+    const float sc = a.scale ? (co_ok ? a.scale[co] : 0.0f) : a.scale_value;
+    const float bi = a.bias ? (co_ok ? a.bias[co] : 0.0f) : 0.0f;
+    const float be = a.beta ? ((scalar_f32_ptr)a.beta)[pix] : 1.0f;
+    store_result(a, pix, co, v, sc, bi, be);
+}
+
+template <int KH, int KW, int CW, int SW, int P>
+hipError_t launch_fast(XArgs a, hipStream_t s, int and_mode)
+{
+    a.strips_per_row = (a.out_w + P - 1) / P;
+    a.strips = (long long)a.n * a.out_h * a.strips_per_row;
+    const long long waves = a.strips * a.tiles;
+    const long long blocks = (waves + 3) / 4;
+    if (waves * 4 >= 0x7fffffffLL) return hipErrorInvalidValue;
+    if (and_mode)
+        hipLaunchKernelGGL((xconv_fast<KH, KW, CW, SW, P, true>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((xconv_fast<KH, KW, CW, SW, P, false>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+// Strip width: 7 when it tiles the row exactly and 8 does not, else 8.
+int strip_width(int out_w) { return (out_w % 8 != 0 && out_w % 7 == 0) ? 7 : 8; }
+
+typedef hipError_t (*fast_launcher)(XArgs, hipStream_t, int);
+
+struct FastEntry {
+    int kh, kw, cw, sw, p;
+    fast_launcher fn;
+    const char *name;
+};
+
+#define BCONV_FAST(KH, KW, CW, SW, P)                                        \
+    {KH, KW, CW, SW, P, &launch_fast<KH, KW, CW, SW, P>,                     \
+     "xconv_fast<" #KH "," #KW "," #CW "," #SW "," #P ">"}
+#define BCONV_FAST_P(KH, KW, CW, SW) BCONV_FAST(KH, KW, CW, SW, 8), BCONV_FAST(KH, KW, CW, SW, 7)
+
+const FastEntry kFast[] = {
+    BCONV_FAST_P(3, 3, 1, 1), BCONV_FAST_P(3, 3, 2, 1), BCONV_FAST_P(3, 3, 3, 1),
+    BCONV_FAST_P(3, 3, 4, 1), BCONV_FAST_P(3, 3, 8, 1),
+    BCONV_FAST_P(3, 3, 1, 2), BCONV_FAST_P(3, 3, 2, 2), BCONV_FAST_P(3, 3, 4, 2),
+    BCONV_FAST_P(3, 3, 8, 2),
+    BCONV_FAST_P(1, 1, 1, 1), BCONV_FAST_P(1, 1, 2, 1), BCONV_FAST_P(1, 1, 4, 1),
+    BCONV_FAST_P(1, 1, 8, 1),
+    BCONV_FAST_P(5, 5, 1, 1), BCONV_FAST_P(5, 5, 2, 1),
+};
+#undef BCONV_FAST_P
+#undef BCONV_FAST
+
+const FastEntry *find_fast(const Geom &g)
+{
+    // The halo must equal the padding on both axes (it does by construction)
+    // and a strip must not be wider than needed for tiny outputs.
+    const int p = strip_width(g.out_w);
+    for (const FastEntry &e : kFast)
+        if (e.kh == g.kh && e.kw == g.kw && e.cw == g.words && e.sw == g.sw && e.p == p) return &e;
+    return nullptr;
+}
+
+XArgs make_args(const Geom &g, const uint32_t *bits, const LaneWeights &w, const Epilogue &e,
+                float *out, int32_t *acc_out)
+{
+    XArgs a{};
+    a.bits = bits;
+    a.wlane = w.words;
+    a.wrect = w.rect;
+    a.scale = e.scale;
+    a.bias = e.bias;
+    a.beta = e.beta;
+    a.scale_value = e.scale_value;
+    a.relu = e.relu;
+    a.out = out;
+    a.acc_out = acc_out;
+    a.n = g.n;
+    a.in_h = g.in_h;
+    a.in_w = g.in_w;
+    a.in_c = g.in_c;
+    a.out_c = g.out_c;
+    a.out_h = g.out_h;
+    a.out_w = g.out_w;
+    a.kh = g.kh;
+    a.kw = g.kw;
+    a.sh = g.sh;
+    a.sw = g.sw;
+    a.ph = g.ph;
+    a.pw = g.pw;
+    a.words = g.words;
+    a.rows = g.bits_rows;
+    a.cols = g.bits_cols;
+    a.kwc4 = w.kwc4;
+    a.tiles = g.tiles;
+    return a;
+}
+
+}  // namespace
+
+int xconv_strip_width(const Geom &g) { return strip_width(g.out_w); }
+
+bool xconv_fast_available(const Geom &g) { return find_fast(g) != nullptr; }
+
+const char *xconv_kernel_name(const Geom &g)
+{
+    const FastEntry *e = find_fast(g);
+    return e ? e->name : "xconv_generic";
+}
+
+hipError_t launch_xconv(const Geom &g, hipStream_t s, int and_mode, const uint32_t *bits,
+                        const LaneWeights &w, const Epilogue &e, float *out, int32_t *acc_out,
+                        bool allow_fast)
+{
+    XArgs a = make_args(g, bits, w, e, out, acc_out);
+    const FastEntry *f = allow_fast ? find_fast(g) : nullptr;
+    if (f) return f->fn(a, s, and_mode);
+    const long long waves = (long long)g.n * g.out_h * g.out_w * g.tiles;
+    const long long blocks = (waves + 3) / 4;
+    if (blocks == 0) return hipSuccess;
+    if (waves * 4 >= 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(xconv_generic, dim3((unsigned)blocks), dim3(256), 0, s, a, and_mode);
+    return hipGetLastError();
+}
+
+}  // namespace bconv

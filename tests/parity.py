@@ -1,0 +1,161 @@
+"""Helpers shared by the GPU parity tests: run a layer through the C ABI,
+run the oracle on the same host arrays, and compare.
+
+Comparison rules (the oracle is float64 and exact; the HIP path is fp32):
+  * XNOR / AND window sums: bit-exact.
+  * packed input bits: bit-exact against the oracle's binarised input.
+  * A map and beta image: relative 1e-5 (sums of non-negative terms).
+  * final outputs, XNOR / AND: |g - o| <= 1e-5 * (|acc*scale*beta| + |bias|).
+  * binaryWeights sums: |g - o| <= 1e-5 * S, S = sum of |x'| over the window;
+    final outputs |g - o| <= 1e-5 * (|scale*beta| * S + |bias|).
+A purely elementwise relative test is ill-posed where a sum cancels, so the
+float bounds are normwise in the terms of each sum.
+"""
+
+from __future__ import annotations
+
+import os
+from contextlib import contextmanager
+
+import numpy as np
+import torch
+
+import oracle
+import popcount_convolution_amd as pca
+from popcount_convolution_amd import workloads
+
+RTOL = 1e-5
+TINY = 1e-30
+
+
+@contextmanager
+def force_generic(on: bool):
+    """Handles created inside use the generic convolution kernel."""
+    old = os.environ.get("BCONV_FORCE_GENERIC")
+    os.environ["BCONV_FORCE_GENERIC"] = "1" if on else "0"
+    try:
+        yield
+    finally:
+        if old is None:
+            os.environ.pop("BCONV_FORCE_GENERIC", None)
+        else:
+            os.environ["BCONV_FORCE_GENERIC"] = old
+
+
+def slice_inputs(inputs: dict, images) -> dict:
+    out = dict(inputs)
+    out["x"] = np.ascontiguousarray(inputs["x"][images])
+    return out
+
+
+def run_gpu(layer: workloads.Layer, inputs: dict, device, generic: bool = False) -> dict:
+    """Forward and forward_accum through the C ABI; also returns the
+    workspace intermediates (bits, A map, beta) of the forward call."""
+    with force_generic(generic):
+        conv = pca.BinaryConvolution.from_layer(layer, inputs)
+    try:
+        n = inputs["x"].shape[0]
+        x = torch.from_numpy(inputs["x"]).to(device)
+        ws = conv.workspace(n, device)
+        ws.fill_(0xA5)  # poison: every byte the kernels rely on must be written
+        shape = (n, conv.out_h, conv.out_w, conv.out_c)
+        out = torch.full(shape, float("nan"), dtype=torch.float32, device=device)
+        if layer.type == "binary_weights":
+            acc = torch.full(shape, float("nan"), dtype=torch.float32, device=device)
+        else:
+            acc = torch.full(shape, -(2 ** 31), dtype=torch.int32, device=device)
+        conv.forward_accum(x, acc, ws)
+        conv.forward(x, out, ws)
+        torch.cuda.synchronize()
+        res = {"out": out.cpu().numpy(), "acc": acc.cpu().numpy(),
+               "main_kernel": conv.main_kernel(n)}
+        L = pca.bconv_workspace_layout(conv.handle, n)
+        wsh = ws.cpu().numpy()
+        if L["bits_offset"] is not None:
+            cnt = n * L["bits_rows"] * L["bits_cols"] * L["bits_words"]
+            words = wsh[L["bits_offset"]:L["bits_offset"] + 4 * cnt].view("<u4")
+            res["bits"] = words.reshape(n, L["bits_rows"], L["bits_cols"], L["bits_words"])
+            res["bits_pad"] = (L["bits_pad_h"], L["bits_pad_w"])
+        if L["a_map_offset"] is not None:
+            res["a_map"] = wsh[L["a_map_offset"]:L["a_map_offset"] + 4 * n * layer.in_h * layer.in_w] \
+                .view("<f4").reshape(n, layer.in_h, layer.in_w)
+            nb = n * conv.out_h * conv.out_w
+            res["beta"] = wsh[L["beta_offset"]:L["beta_offset"] + 4 * nb].view("<f4") \
+                .reshape(n, conv.out_h, conv.out_w)
+        return res
+    finally:
+        conv.close()
+
+
+def expected_words(signs: np.ndarray, form: str) -> np.ndarray:
+    """Pack the oracle's binarised input into little-endian uint32 words,
+    channel c at bit c%32 of word c//32, zero tail bits."""
+    bits = (signs > 0).astype(np.uint8)
+    n, h, w, c = bits.shape
+    words = (c + 31) // 32
+    padded = np.zeros((n, h, w, words * 32), np.uint8)
+    padded[..., :c] = bits
+    packed = np.packbits(padded, axis=-1, bitorder="little")
+    return packed.view("<u4").reshape(n, h, w, words)
+
+
+def window_abs_sum(layer: workloads.Layer, inputs: dict) -> np.ndarray:
+    """S[n,oy,ox] = sum of |x'| over the in-image taps of the window (float64)."""
+    x = inputs["x"].astype(np.float64)
+    if inputs.get("input_scale") is not None:
+        x = x * inputs["input_scale"].astype(np.float64)
+    if inputs.get("input_bias") is not None:
+        x = x + inputs["input_bias"].astype(np.float64)
+    a = np.abs(x).sum(axis=-1)[:, None]
+    k = torch.ones((1, 1, layer.kernel_h, layer.kernel_w), dtype=torch.float64)
+    s = torch.nn.functional.conv2d(torch.from_numpy(a), k, stride=(layer.stride_h, layer.stride_w),
+                                   padding=(layer.pad_h, layer.pad_w))
+    return s.numpy()[:, 0]
+
+
+def compare(layer: workloads.Layer, inputs: dict, got: dict, ref: dict = None, images=None) -> dict:
+    """Assert the GPU results (optionally only on `images`) match the oracle."""
+    sub = inputs if images is None else slice_inputs(inputs, images)
+    if ref is None:
+        ref = oracle.bconv_layer(layer, sub)
+    g = {k: (v if images is None or not isinstance(v, np.ndarray) else v[images])
+         for k, v in got.items()}
+    oc = layer.out_c
+    scale = (sub["output_scale"].astype(np.float64) if sub.get("output_scale") is not None
+             else np.full(oc, layer.scale_value, np.float64))
+    bias = (sub["output_bias"].astype(np.float64) if sub.get("output_bias") is not None
+            else np.zeros(oc))
+    beta = ref["beta"][..., None]
+    if layer.type == "binary_weights":
+        S = window_abs_sum(layer, sub)[..., None]
+        err = np.abs(g["acc"].astype(np.float64) - ref["acc"])
+        assert np.all(err <= RTOL * S + TINY), f"{layer.name}: binaryWeights sums off by {err.max()}"
+        bound = RTOL * (np.abs(scale * beta) * S + np.abs(bias)) + TINY
+    else:
+        if not np.array_equal(g["acc"], ref["acc"]):
+            bad = np.argwhere(g["acc"] != ref["acc"])
+            i = tuple(bad[0])
+            raise AssertionError(f"{layer.name}: {len(bad)} window sums differ, first at {i}: "
+                                 f"gpu {g['acc'][i]} oracle {ref['acc'][i]}")
+        bound = RTOL * (np.abs(ref["acc"] * scale * beta) + np.abs(bias)) + TINY
+    err = np.abs(g["out"].astype(np.float64) - ref["out"])
+    ok = err <= bound
+    if not np.all(ok):
+        i = tuple(np.argwhere(~ok)[0])
+        raise AssertionError(f"{layer.name}: {np.count_nonzero(~ok)} outputs beyond tolerance, "
+                             f"first at {i}: gpu {g['out'][i]} oracle {ref['out'][i]}")
+    if "bits" in g and ref.get("signs") is not None:
+        ph, pw = got["bits_pad"]
+        h, w = layer.in_h, layer.in_w
+        inner = g["bits"][:, ph:ph + h, pw:pw + w, :]
+        want = expected_words(ref["signs"], layer.type)
+        assert np.array_equal(inner, want), f"{layer.name}: packed input bits differ"
+        halo = g["bits"].copy()
+        halo[:, ph:ph + h, pw:pw + w, :] = 0
+        assert not halo.any(), f"{layer.name}: halo of the packed input is not zero"
+    if layer.use_beta:
+        np.testing.assert_allclose(g["a_map"], ref["a_map"], rtol=RTOL, atol=0,
+                                   err_msg=f"{layer.name}: A map")
+        np.testing.assert_allclose(g["beta"], ref["beta"], rtol=RTOL, atol=0,
+                                   err_msg=f"{layer.name}: beta")
+    return ref

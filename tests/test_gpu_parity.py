@@ -1,0 +1,228 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Every case draws seeded host inputs once; the same arrays feed the GPU and the
+oracle.  Integer window sums and packed bits must be bit-exact; float results
+follow the normwise bounds documented in ``parity.py``.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import parity
+import popcount_convolution_amd as pca
+from popcount_convolution_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    pca.load_library()
+    return torch.device("cuda:0")
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+# ------------------------------------------------------------ measured layers
+
+@pytest.mark.parametrize("index", range(len(workloads.LAYERS)),
+                         ids=[l.name for l in workloads.LAYERS])
+def test_measured_layer_sampled(dev, index):
+    """Each measured layer at full size, in the launch configuration the
+    benchmark times; the oracle checks the first and last images (all of a
+    single-image layer), FC rows 0, 1 and the last."""
+    layer = workloads.LAYERS[index]
+    inputs = workloads.make_inputs(layer, workloads.layer_seed(index))
+    _log(f"layer {layer.name} seed {workloads.layer_seed(index)}")
+    got = parity.run_gpu(layer, inputs, dev)
+    n = layer.n
+    images = sorted({0, 1, n - 1}) if layer.is_fc else sorted({0, n - 1})
+    parity.compare(layer, inputs, got, images=np.array(images))
+
+
+def test_small_layer_full(dev):
+    """The single-image layer compared on every output, fast and generic paths."""
+    layer = workloads.LAYERS[0]
+    inputs = workloads.make_inputs(layer, workloads.layer_seed(0))
+    ref = oracle.bconv_layer(layer, inputs)
+    for generic in (False, True):
+        got = parity.run_gpu(layer, inputs, dev, generic=generic)
+        parity.compare(layer, inputs, got, ref=ref)
+
+
+def test_bench_layer_two_full_images(dev):
+    """The benchmark layer (XNOR + beta + affine + ReLU) on two whole images,
+    every output, fast and generic kernels."""
+    layer = workloads.BENCH_LAYER.with_(n=2)
+    inputs = workloads.make_inputs(layer, 77)
+    ref = oracle.bconv_layer(layer, inputs)
+    for generic in (False, True):
+        got = parity.run_gpu(layer, inputs, dev, generic=generic)
+        parity.compare(layer, inputs, got, ref=ref)
+
+
+# ---------------------------------------------------------------- sweeps
+
+def _sweep_layers():
+    """Geometries that span several channel tiles and strips with ragged
+    tails, every word-count tail, all strides/paddings the kernels special-
+    case, 1x1 / 2x2 / 3x3 / 5x5 kernels and the FC shape."""
+    base = workloads.Layer("sweep", "xnor", 2, 9, 10, 64, 70, 3, 3, 1, 1, 1, 1)
+    geoms = [
+        dict(n=3, in_h=11, in_w=19, in_c=128, out_c=130),             # 3 tiles, ragged strips
+        dict(n=1, in_h=5, in_w=7, in_c=33, out_c=65),
+        dict(n=2, in_h=8, in_w=8, in_c=100, out_c=1),
+        dict(n=2, in_h=14, in_w=14, in_c=256, out_c=64, stride_h=2, stride_w=2),
+        dict(n=1, in_h=13, in_w=9, in_c=96, out_c=40, stride_h=2, stride_w=2, pad_h=0, pad_w=0),
+        dict(n=2, in_h=6, in_w=21, in_c=31, out_c=17),
+        dict(n=1, in_h=1, in_w=1, in_c=64, out_c=8),                  # every tap but one padded
+        dict(n=2, in_h=9, in_w=9, in_c=1, out_c=3),                   # Cin = 1
+        dict(n=2, in_h=10, in_w=12, in_c=64, out_c=64, kernel_h=1, kernel_w=1, pad_h=0, pad_w=0),
+        dict(n=1, in_h=9, in_w=9, in_c=160, out_c=64, kernel_h=1, kernel_w=1, pad_h=0, pad_w=0,
+             stride_h=2, stride_w=3),
+        dict(n=2, in_h=12, in_w=11, in_c=64, out_c=33, kernel_h=5, kernel_w=5, pad_h=2, pad_w=2),
+        dict(n=1, in_h=10, in_w=10, in_c=32, out_c=20, kernel_h=5, kernel_w=5, pad_h=1, pad_w=3),
+        dict(n=2, in_h=7, in_w=8, in_c=45, out_c=9, kernel_h=2, kernel_w=2, pad_h=1, pad_w=1),
+        dict(n=1, in_h=9, in_w=10, in_c=70, out_c=5, kernel_h=3, kernel_w=1, pad_h=1, pad_w=0,
+             stride_h=3, stride_w=1),
+        dict(n=3, in_h=4, in_w=5, in_c=37, out_c=66, kernel_h=4, kernel_w=5, pad_h=0, pad_w=0),  # FC
+        dict(n=2, in_h=3, in_w=3, in_c=512, out_c=100, kernel_h=3, kernel_w=3, pad_h=0, pad_w=0),  # FC
+        dict(n=1, in_h=16, in_w=16, in_c=96, out_c=64),
+        dict(n=1, in_h=8, in_w=56, in_c=128, out_c=128),
+        dict(n=1, in_h=7, in_w=28, in_c=256, out_c=256),
+    ]
+    out = []
+    for gi, gd in enumerate(geoms):
+        for form in ("xnor", "and", "binary_weights"):
+            for variant in range(2):
+                kw = dict(gd)
+                kw["type"] = form
+                kw["name"] = f"g{gi}_{form}_v{variant}"
+                if variant == 1:
+                    kw.update(use_beta=True, neuron="relu", iscale_dist=("uniform", 0.5, 1.5),
+                              ibias_dist=("normal", 0.0, 0.2))
+                if (gi + variant) % 3 == 2:
+                    kw.update(oscale_dist=None, obias_dist=None, scale_value=0.75)
+                out.append(base.with_(**kw))
+    return out
+
+
+SWEEP = _sweep_layers()
+
+
+@pytest.mark.parametrize("layer", SWEEP, ids=[l.name for l in SWEEP])
+def test_sweep(dev, layer):
+    inputs = workloads.make_inputs(layer, 5000 + SWEEP.index(layer))
+    _log(f"sweep {layer}")
+    ref = oracle.bconv_layer(layer, inputs)
+    got = parity.run_gpu(layer, inputs, dev)
+    parity.compare(layer, inputs, got, ref=ref)
+    if layer.type != "binary_weights":
+        gen = parity.run_gpu(layer, inputs, dev, generic=True)
+        parity.compare(layer, inputs, gen, ref=ref)
+
+
+def test_special_values(dev):
+    """Signed zeros, NaN, subnormals and exact ties of the input affine
+    binarise as the oracle says (x' < 0 -> -1, else +1)."""
+    layer = workloads.Layer("special", "xnor", 1, 4, 4, 64, 64, 3, 3, 1, 1, 1, 1)
+    inputs = workloads.make_inputs(layer, 91)
+    x = inputs["x"]
+    specials = np.array([0.0, -0.0, np.nan, 1e-40, -1e-40, -1e-45, 1e-45, -np.inf, np.inf],
+                        np.float32)
+    flat = x.reshape(-1)
+    flat[: specials.size * 7: 7] = np.resize(specials, flat[: specials.size * 7: 7].shape)
+    inputs["x"] = x
+    for form in ("xnor", "and"):
+        ly = layer.with_(type=form)
+        got = parity.run_gpu(ly, inputs, dev)
+        ref = oracle.bconv_layer(ly, inputs)
+        assert np.array_equal(got["acc"], ref["acc"])
+        ph, pw = got["bits_pad"]
+        assert np.array_equal(got["bits"][:, ph:ph + 4, pw:pw + 4], parity.expected_words(ref["signs"], form))
+
+
+# ------------------------------------------------------------ robustness
+
+def test_repeat_is_bit_identical(dev):
+    layer = workloads.BENCH_LAYER.with_(n=2)
+    inputs = workloads.make_inputs(layer, 3)
+    a = parity.run_gpu(layer, inputs, dev)
+    b = parity.run_gpu(layer, inputs, dev)
+    assert np.array_equal(a["out"].view(np.uint32), b["out"].view(np.uint32))
+    assert np.array_equal(a["beta"].view(np.uint32), b["beta"].view(np.uint32))
+
+
+def test_two_streams_share_a_handle(dev):
+    layer = workloads.LAYERS[2].with_(n=4)
+    inputs = workloads.make_inputs(layer, 4)
+    conv = pca.BinaryConvolution.from_layer(layer, inputs)
+    try:
+        x = torch.from_numpy(inputs["x"]).to(dev)
+        s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+        ws1, ws2 = conv.workspace(4, dev), conv.workspace(4, dev)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s1):
+            o1 = conv.forward(x, workspace=ws1, stream=s1)
+        with torch.cuda.stream(s2):
+            o2 = conv.forward(x, workspace=ws2, stream=s2)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2)
+    finally:
+        conv.close()
+
+
+def test_argument_errors(dev):
+    layer = workloads.BENCH_LAYER.with_(n=2)
+    inputs = workloads.make_inputs(layer, 5)
+    conv = pca.BinaryConvolution.from_layer(layer, inputs)
+    try:
+        x = torch.from_numpy(inputs["x"]).to(dev)
+        out = torch.empty((2, 56, 56, 128), device=dev)
+        need = conv.workspace_bytes(2)
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        s = torch.cuda.current_stream().cuda_stream
+        with pytest.raises(pca.BconvError) as e:
+            pca.bconv_forward(conv.handle, s, 2, x, out, ws, need - 1)
+        assert e.value.status == pca.BCONV_ERR_WORKSPACE
+        with pytest.raises(pca.BconvError) as e:
+            pca.bconv_forward(conv.handle, s, 2, x, x, ws, need)
+        assert e.value.status == pca.BCONV_ERR_INVALID_ARGUMENT
+        with pytest.raises(pca.BconvError) as e:
+            pca.bconv_forward(conv.handle, s, -1, x, out, ws, need)
+        assert e.value.status == pca.BCONV_ERR_INVALID_ARGUMENT
+        out.fill_(3.0)
+        pca.bconv_forward(conv.handle, s, 0, x, out, None, 0)  # empty batch: no-op
+        torch.cuda.synchronize()
+        assert bool((out == 3.0).all())
+    finally:
+        conv.close()
+
+
+def test_fc_entry_point_matches_conv(dev):
+    """bconv_create_fc builds the same layer as bconv_create with kernel =
+    source size; outputs are identical."""
+    layer = workloads.LAYERS[4].with_(n=8, out_c=300)
+    inputs = workloads.make_inputs(layer, 12)
+    conv = pca.BinaryConvolution.from_layer(layer, inputs)
+    h = pca.bconv_create_fc(7, 7, 512, 300, pca.BCONV_NEURON_NONE, 1.0, inputs["weight_bits"],
+                            inputs["output_scale"], inputs["output_bias"], None, None, pca.BCONV_XNOR,
+                            pca.BCONV_FLAG_NONE)
+    try:
+        x = torch.from_numpy(inputs["x"]).to(dev)
+        a = conv.forward(x)
+        b = torch.empty_like(a)
+        ws = torch.empty(max(1, pca.bconv_workspace_size(h, 8)), dtype=torch.uint8, device=dev)
+        pca.bconv_forward(h, torch.cuda.current_stream().cuda_stream, 8, x, b, ws, ws.numel())
+        torch.cuda.synchronize()
+        assert torch.equal(a, b)
+        assert pca.bconv_get_info(h) == (512, 300, 1, 1)
+    finally:
+        pca.bconv_destroy(h)
+        conv.close()
