@@ -107,11 +107,13 @@ typedef struct {
 /* Where the per-step intermediates sit in a forward call's workspace, for
  * checking each step on its own.  Offsets are in bytes from the workspace
  * start; SIZE_MAX marks a section the handle does not use.
- *   bits: uint32 [n][bits_rows][bits_cols][bits_words], the binarised input
- *         with a zero halo of bits_pad_h rows and bits_pad_w columns on each
- *         side; channel f of pixel (y,x) is bit (f%32) of word f/32 at
- *         row y + bits_pad_h, column x + bits_pad_w.
- *   a_map: float [n][in_h][in_w];  beta: float [n][out_h][out_w]. */
+ *   bits:  uint32 [n][bits_rows][bits_cols][bits_words], the binarised input
+ *          with a zero halo of bits_pad_h rows and bits_pad_w columns on each
+ *          side; channel f of pixel (y,x) is bit (f%32) of word f/32 at row
+ *          y + bits_pad_h, column x + bits_pad_w (XNOR and AND only).
+ *   a_map: float [n][bits_rows][bits_cols], the A map with the same zero halo
+ *          (only with BCONV_FLAG_USE_BETA_SCALING).
+ *   beta:  float [n][out_h][out_w] (only with BCONV_FLAG_USE_BETA_SCALING). */
 typedef struct {
     size_t bits_offset;
     int32_t bits_rows, bits_cols, bits_words, bits_pad_h, bits_pad_w;

@@ -19,6 +19,7 @@ struct bconv_handle {
     uint32_t flags;
     int device;
     int out_h, out_w, words, tiles;
+    int simds;                // SIMD units of the device
     bool force_generic;
     bconv::LaneWeights lane;  // XNOR / AND
     uint32_t *d_lane_words;
@@ -104,6 +105,7 @@ bconv::Geom make_geom(const bconv_handle *h, int n)
     g.out_w = h->out_w;
     g.words = h->words;
     g.tiles = h->tiles;
+    g.simds = h->simds;
     g.bits_halo_h = d.pad_h;
     g.bits_halo_w = d.pad_w;
     g.bits_rows = d.in_h + 2 * d.pad_h;
@@ -134,8 +136,14 @@ bconv_workspace_layout_t layout_for(const bconv_handle *h, int n)
         off = align_up(off + words * 4);
     }
     if (uses_beta(h) && n > 0) {
+        // A map with the same zero halo as the bit buffer; beta as written by
+        // the convolution kernels.
         L.a_map_offset = off;
-        off = align_up(off + (size_t)n * g.in_h * g.in_w * 4);
+        L.bits_rows = g.bits_rows;
+        L.bits_cols = g.bits_cols;
+        L.bits_pad_h = g.bits_halo_h;
+        L.bits_pad_w = g.bits_halo_w;
+        off = align_up(off + (size_t)n * g.bits_rows * g.bits_cols * 4);
         L.beta_offset = off;
         off = align_up(off + (size_t)n * g.out_h * g.out_w * 4);
     }
@@ -204,6 +212,8 @@ bconv_status_t forward_impl(bconv_t h, void *stream, int32_t n, const float *in,
     const size_t out_bytes = (size_t)n * h->out_h * h->out_w * d.out_c * 4;
     if (ranges_overlap(in, in_bytes, dst, out_bytes))
         return fail(BCONV_ERR_INVALID_ARGUMENT, "input and output overlap");
+    if ((long long)n * d.in_h * d.in_w >= (1LL << 31) || (long long)n * h->out_h * h->out_w * h->tiles >= (1LL << 29))
+        return fail(BCONV_ERR_INVALID_ARGUMENT, "batch too large: pixel indices must fit 31 bits");
     const bconv_workspace_layout_t L = layout_for(h, n);
     if (L.total_bytes > 0 && (!workspace || workspace_bytes < L.total_bytes))
         return fail(BCONV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total_bytes,
@@ -226,35 +236,25 @@ bconv_status_t forward_impl(bconv_t h, void *stream, int32_t n, const float *in,
         e = bconv::launch_pack(g, s, in, h->d_in_scale, h->d_in_bias, bits, a_map);
         if (e != hipSuccess) return hip_fail(e, "pack kernel");
     }
-    if (beta) {
-        e = bconv::launch_beta(g, s, a_map, beta);
-        if (e != hipSuccess) return hip_fail(e, "beta kernel");
-    }
     bconv::Epilogue ep{};
     ep.scale = h->d_out_scale;
     ep.bias = h->d_out_bias;
     ep.scale_value = d.scale_value;
-    ep.beta = beta;
+    ep.a_pad = a_map;
+    ep.beta_out = beta;
     ep.relu = d.neuron == BCONV_NEURON_RELU;
-    if (ev_begin) {
-        e = hipEventRecord(static_cast<hipEvent_t>(ev_begin), s);
-        if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
-    }
+    const bconv::Launch main{s, static_cast<hipEvent_t>(ev_begin), static_cast<hipEvent_t>(ev_end)};
     if (h->type == BCONV_BINARY_WEIGHTS) {
-        e = bconv::launch_bwconv(g, s, in, h->d_in_scale, h->d_in_bias, h->d_pm, h->pm_cols, ep,
+        e = bconv::launch_bwconv(g, main, in, h->d_in_scale, h->d_in_bias, h->d_pm, h->pm_cols, ep,
                                  sink == Sink::Output ? static_cast<float *>(dst) : nullptr,
                                  sink == Sink::Accum ? static_cast<float *>(dst) : nullptr);
     } else {
-        e = bconv::launch_xconv(g, s, h->type == BCONV_AND, bits, h->lane, ep,
+        e = bconv::launch_xconv(g, main, h->type == BCONV_AND, bits, h->lane, ep,
                                 sink == Sink::Output ? static_cast<float *>(dst) : nullptr,
                                 sink == Sink::Accum ? static_cast<int32_t *>(dst) : nullptr,
                                 !h->force_generic);
     }
     if (e != hipSuccess) return hip_fail(e, "convolution kernel");
-    if (ev_end) {
-        e = hipEventRecord(static_cast<hipEvent_t>(ev_end), s);
-        if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
-    }
     return BCONV_OK;
 }
 
@@ -290,10 +290,13 @@ bconv_status_t bconv_create(const bconv_desc_t *desc, const uint32_t *weight_bit
     const char *fg = getenv("BCONV_FORCE_GENERIC");
     h->force_generic = fg && fg[0] == '1';
     hipError_t e = hipGetDevice(&h->device);
+    int cus = 0;
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h->device);
     if (e != hipSuccess) {
         release(h);
         return hip_fail(e, "hipGetDevice");
     }
+    h->simds = 4 * cus;
 
     const int taps = desc->kernel_h * desc->kernel_w;
     const size_t user_words = (size_t)desc->out_c * taps * h->words;

@@ -20,7 +20,10 @@ struct BwArgs {
     const float *x, *in_scale, *in_bias;
     const float *pm;  // [taps*in_c][pm_cols]
     int pm_cols;
-    const float *scale, *bias, *beta;
+    const float *scale, *bias;
+    const float *a_pad;  // zero-halo A map or nullptr (beta = 1)
+    float *beta_out;
+    int rows, cols;
     float scale_value;
     int relu;
     float *out;
@@ -90,21 +93,30 @@ __global__ __launch_bounds__(256) void bwconv_kernel(BwArgs a)
     }
 
     if (!live) return;
-    const float be = a.beta ? a.beta[m] : 1.0f;
+    float be = 1.0f;
+    if (a.a_pad) {
+        // beta: window sum of the zero-halo A map / (kh*kw)
+        const float *ap = a.a_pad + (img * a.rows + (long long)oy * a.sh) * a.cols + (long long)ox * a.sw;
+        float sum = 0.0f;
+        for (int ky = 0; ky < a.kh; ++ky)
+            for (int kx = 0; kx < a.kw; ++kx) sum += ap[ky * a.cols + kx];
+        be = sum / (float)(a.kh * a.kw);
+        if (cb == 0) a.beta_out[m] = be;
+    }
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
         const int co = cb * Q + q;
         if (co >= a.out_c) break;
         const long long o = m * a.out_c + co;
         if (a.acc_out) {
-            a.acc_out[o] = acc[q];
+            __hip_atomic_store(&a.acc_out[o], acc[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             continue;
         }
         const float sc = a.scale ? a.scale[co] : a.scale_value;
         const float bi = a.bias ? a.bias[co] : 0.0f;
         float r = __builtin_fmaf(acc[q] * sc, be, bi);
         if (a.relu) r = (r < 0.0f) ? 0.0f : r;
-        a.out[o] = r;
+        __hip_atomic_store(&a.out[o], r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -119,7 +131,7 @@ const char *bwconv_kernel_name(const Geom &g)
     return (g.in_c % 4 == 0) ? "bwconv_kernel<32,4>" : "bwconv_kernel<32,1>";
 }
 
-hipError_t launch_bwconv(const Geom &g, hipStream_t s, const float *x, const float *in_scale,
+hipError_t launch_bwconv(const Geom &g, const Launch &L, const float *x, const float *in_scale,
                          const float *in_bias, const float *pm_weights, int pm_cols,
                          const Epilogue &e, float *out, float *acc_out)
 {
@@ -131,7 +143,10 @@ hipError_t launch_bwconv(const Geom &g, hipStream_t s, const float *x, const flo
     a.pm_cols = pm_cols;
     a.scale = e.scale;
     a.bias = e.bias;
-    a.beta = e.beta;
+    a.a_pad = e.a_pad;
+    a.beta_out = e.beta_out;
+    a.rows = g.bits_rows;
+    a.cols = g.bits_cols;
     a.scale_value = e.scale_value;
     a.relu = e.relu;
     a.out = out;
@@ -156,11 +171,8 @@ hipError_t launch_bwconv(const Geom &g, hipStream_t s, const float *x, const flo
     if (blocks == 0) return hipSuccess;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
     const bool vec4 = (g.in_c % 4 == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0);
-    if (vec4)
-        hipLaunchKernelGGL((bwconv_kernel<kQ, 4>), dim3((unsigned)blocks), dim3(256), 0, s, a);
-    else
-        hipLaunchKernelGGL((bwconv_kernel<kQ, 1>), dim3((unsigned)blocks), dim3(256), 0, s, a);
-    return hipGetLastError();
+    if (vec4) return launch_kernel(L, bwconv_kernel<kQ, 4>, dim3((unsigned)blocks), dim3(256), 0, a);
+    return launch_kernel(L, bwconv_kernel<kQ, 1>, dim3((unsigned)blocks), dim3(256), 0, a);
 }
 
 }  // namespace bconv

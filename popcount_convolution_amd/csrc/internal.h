@@ -2,6 +2,7 @@
 // libbconv.so.  Not part of the public ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -25,7 +26,26 @@ struct Geom {
     int bits_cols;    // in_w + 2*pw
     int bits_halo_h, bits_halo_w;
     long long bits_slack_words;  // zero words after the last image (strip over-reads)
+    int simds;        // SIMD units of the device (4 per compute unit)
 };
+
+// Stream plus the optional hipEvents that bracket one kernel dispatch: with
+// events, the kernel is launched by hipExtLaunchKernelGGL, which records
+// them at the dispatch's own start and completion.
+struct Launch {
+    hipStream_t stream;
+    hipEvent_t begin, end;
+};
+
+template <typename... Args, typename F>
+hipError_t launch_kernel(const Launch &L, F kernel, dim3 grid, dim3 block, uint32_t lds, Args... args)
+{
+    if (L.begin || L.end)
+        hipExtLaunchKernelGGL(kernel, grid, block, lds, L.stream, L.begin, L.end, 0, args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, lds, L.stream, args...);
+    return hipGetLastError();
+}
 
 // Per-lane weight words, grouped by kernel row: [tiles][kh][kwc4][64][4],
 // kwc4 = ceil(kw*words / 4).  Within row ky, word r = kx*words + w; lane l
@@ -38,33 +58,33 @@ struct LaneWeights {
     int kwc4;
 };
 
-// Epilogue operands.
+// Epilogue operands.  With a_pad set, the convolution kernels form beta as
+// the window sum of the zero-halo A map / (kh*kw) and also store it to
+// beta_out ([n][out_h][out_w]); without it beta is 1.
 struct Epilogue {
     const float *scale;  // [out_c] or nullptr -> scale_value
     const float *bias;   // [out_c] or nullptr -> 0
     float scale_value;
-    const float *beta;   // [n][out_h][out_w] or nullptr -> 1
+    const float *a_pad;  // [n][bits_rows][bits_cols] or nullptr
+    float *beta_out;     // [n][out_h][out_w] (used when a_pad is set)
     int relu;
 };
 
 // Launchers (each returns the hipGetLastError() of its launch).
 hipError_t launch_pack(const Geom &g, hipStream_t s, const float *x, const float *in_scale,
                        const float *in_bias, uint32_t *bits, float *a_map);
-hipError_t launch_beta(const Geom &g, hipStream_t s, const float *a_map, float *beta);
 hipError_t launch_prepack(const Geom &g, hipStream_t s, const uint32_t *user_bits, uint32_t *lane_words,
                           int32_t *lane_popc, float *pm_weights, int pm_cols, int type);
 // Returns true when a specialised convolution kernel exists for this shape.
 bool xconv_fast_available(const Geom &g);
-// Output pixels per strip of the specialised kernel (sizes the over-read slack).
-int xconv_strip_width(const Geom &g);
 const char *xconv_kernel_name(const Geom &g);
-hipError_t launch_xconv(const Geom &g, hipStream_t s, int and_mode, const uint32_t *bits,
+hipError_t launch_xconv(const Geom &g, const Launch &L, int and_mode, const uint32_t *bits,
                         const LaneWeights &w, const Epilogue &e, float *out, int32_t *acc_out,
                         bool allow_fast);
 // Columns of the +-1.0f binaryWeights table (out_c rounded up to the channel block).
 int bwconv_pm_cols(int out_c);
 const char *bwconv_kernel_name(const Geom &g);
-hipError_t launch_bwconv(const Geom &g, hipStream_t s, const float *x, const float *in_scale,
+hipError_t launch_bwconv(const Geom &g, const Launch &L, const float *x, const float *in_scale,
                          const float *in_bias, const float *pm_weights, int pm_cols,
                          const Epilogue &e, float *out, float *acc_out);
 

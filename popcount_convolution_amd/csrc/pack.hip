@@ -1,9 +1,10 @@
-// Binarise-and-pack of the input, with the fused A map, and the beta box
-// filter.
+// Binarise-and-pack of the input, with the fused A map.
 //
 // Input affine and sign: Apple "MPSCNNBinaryConvolution", Overview (input
-// terms paragraph; XNOR and AND bullets).  A map and beta: same page, the two
-// beta equations.
+// terms paragraph; XNOR and AND bullets).  A map: same page, second beta
+// equation (mean over channels of |in'|).  The A map is written with the
+// same zero halo as the bit buffer, so the convolution kernels form beta (the
+// window sum of A over kh*kw, first beta equation) without bounds checks.
 #include "internal.h"
 
 namespace bconv {
@@ -14,7 +15,7 @@ struct PackArgs {
     const float *in_scale;  // [in_c] or nullptr
     const float *in_bias;   // [in_c] or nullptr
     uint32_t *bits;         // padded bit buffer or nullptr (A only)
-    float *a_map;           // [pixels] or nullptr
+    float *a_map;           // padded [n][rows][cols] or nullptr
     long long pixels;       // n*in_h*in_w
     int in_h, in_w, in_c, words;
     int rows, cols, halo_h, halo_w;
@@ -23,41 +24,182 @@ struct PackArgs {
     long long halo_words;   // n*halo_pixels_per_image*words
     long long slack_words;  // zero words after the last image
     long long image_words;  // rows*cols*words
+    long long halo_a;       // n*halo_pixels_per_image (A map halo entries)
     int n;
 };
 
-// Zero the halo of every image and the slack after the last image, so that
-// padded taps and strip over-reads see 0 bits.
-__device__ void clear_halo(const PackArgs &a, long long t)
+__device__ __forceinline__ void halo_pixel(const PackArgs &a, unsigned i, int &row, int &col)
 {
-    if (t >= a.halo_words + a.slack_words) return;
-    if (t >= a.halo_words) {
-        a.bits[(long long)a.n * a.image_words + (t - a.halo_words)] = 0u;
-        return;
-    }
-    const long long per_image = a.halo_pixels_per_image * a.words;
-    const long long img = t / per_image;
-    long long r = t % per_image;
-    const int word = (int)(r % a.words);
-    long long i = r / a.words;  // halo pixel within the image
-    int row, col;
-    const long long top = (long long)a.halo_h * a.cols;
-    const long long bottom = (long long)(a.rows - a.halo_h - a.in_h) * a.cols;
+    const unsigned cols = (unsigned)a.cols;
+    const unsigned top = (unsigned)a.halo_h * cols;
+    const unsigned bottom = (unsigned)(a.rows - a.halo_h - a.in_h) * cols;
     if (i < top) {
-        row = (int)(i / a.cols);
-        col = (int)(i % a.cols);
+        row = (int)(i / cols);
+        col = (int)(i % cols);
     } else if (i - top < bottom) {
         i -= top;
-        row = a.halo_h + a.in_h + (int)(i / a.cols);
-        col = (int)(i % a.cols);
+        row = a.halo_h + a.in_h + (int)(i / cols);
+        col = (int)(i % cols);
     } else {
         i -= top + bottom;
-        const int side = a.cols - a.in_w;
+        const unsigned side = (unsigned)(a.cols - a.in_w);
         row = a.halo_h + (int)(i / side);
         const int j = (int)(i % side);
         col = j < a.halo_w ? j : a.in_w + j;
     }
-    a.bits[img * a.image_words + ((long long)row * a.cols + col) * a.words + word] = 0u;
+}
+
+// Zero the halo of every image (bit words, then A entries) and the slack
+// after the last image, so that padded taps and strip over-reads see 0.
+__device__ void clear_halo(const PackArgs &a, long long t)
+{
+    // halo and slack counts fit 31 bits (they are below the padded buffer size)
+    if (t >= a.halo_words + a.slack_words) {
+        const unsigned u = (unsigned)(t - a.halo_words - a.slack_words);
+        if ((long long)u >= a.halo_a) return;
+        const unsigned per = (unsigned)a.halo_pixels_per_image;
+        const unsigned img = u / per;
+        int row, col;
+        halo_pixel(a, u - img * per, row, col);
+        a.a_map[((long long)img * a.rows + row) * a.cols + col] = 0.0f;
+        return;
+    }
+    if (t >= a.halo_words) {
+        a.bits[(long long)a.n * a.image_words + (t - a.halo_words)] = 0u;
+        return;
+    }
+    const unsigned u = (unsigned)t;
+    const unsigned per_image = (unsigned)(a.halo_pixels_per_image * a.words);
+    const unsigned img = u / per_image;
+    const unsigned r = u - img * per_image;
+    const unsigned word = r % (unsigned)a.words;
+    int row, col;
+    halo_pixel(a, r / (unsigned)a.words, row, col);
+    a.bits[(long long)img * a.image_words + ((long long)row * a.cols + col) * a.words + word] = 0u;
+}
+
+// Pixel indices fit 31 bits (the host checks), so the decomposition uses
+// 32-bit divisions; 64-bit ones expand to long VALU sequences.
+__device__ __forceinline__ long long padded_pixel(const PackArgs &a, long long pix)
+{
+    const unsigned p = (unsigned)pix;
+    const unsigned hw = (unsigned)a.in_h * (unsigned)a.in_w;
+    const unsigned img = p / hw;
+    const unsigned rem = p - img * hw;
+    const unsigned y = rem / (unsigned)a.in_w;
+    const unsigned x = rem - y * (unsigned)a.in_w;
+    return ((long long)img * a.rows + y + a.halo_h) * a.cols + x + a.halo_w;
+}
+
+// DPP lane exchanges within rows of 16 lanes (gfx9 encodings).
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within 8
+constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within 16
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// OR over aligned groups of N lanes (N <= 8); every lane gets its group's OR.
+template <int N>
+__device__ __forceinline__ uint32_t group_or(uint32_t v)
+{
+    if (N >= 2) v |= dpp_u32<kDppXor1>(v);
+    if (N >= 4) v |= dpp_u32<kDppXor2>(v);
+    if (N >= 8) v |= dpp_u32<kDppHalfMirror>(v);
+    return v;
+}
+// Sum over aligned groups of N lanes (N <= 64), in a fixed order.
+template <int N>
+__device__ __forceinline__ float group_sum(float v)
+{
+    if (N >= 2) v += dpp_f32<kDppXor1>(v);
+    if (N >= 4) v += dpp_f32<kDppXor2>(v);
+    if (N >= 8) v += dpp_f32<kDppHalfMirror>(v);
+    if (N >= 16) v += dpp_f32<kDppMirror>(v);
+    if (N >= 32) v += __shfl_xor(v, 16, 64);
+    if (N >= 64) v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
+// Fast path: in_c % 4 == 0 and a 16-byte aligned input.  A pixel's channels
+// are spread over SEG lanes, four consecutive channels (one float4) per lane
+// and SEG*4 channels per chunk; a wave pass covers 64/SEG pixels and a wave
+// makes U passes over consecutive pixels with all U loads issued first.  The
+// input scale and bias of a lane's channels are loaded once per chunk.  A
+// 32-channel word is the OR of 8 lanes' 4-bit groups (DPP), |x'| is summed
+// per lane and then over the pixel's lanes in a fixed order.
+template <int SEG, int U>
+__global__ __launch_bounds__(256) void pack_vec4(PackArgs a)
+{
+    if ((int)blockIdx.x >= a.pack_blocks) {
+        clear_halo(a, (long long)(blockIdx.x - a.pack_blocks) * blockDim.x + threadIdx.x);
+        return;
+    }
+    constexpr int G = 64 / SEG;
+    constexpr int LPW = SEG < 8 ? SEG : 8;
+    const int lane = threadIdx.x & 63;
+    const int slot = lane / SEG;
+    const int sl = lane % SEG;
+    const long long wave = (long long)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    const long long pix0 = wave * (G * U) + slot;
+    const bool affine = a.in_scale != nullptr || a.in_bias != nullptr;
+    float asum[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) asum[u] = 0.0f;
+    for (int c0 = 0; c0 < a.in_c; c0 += SEG * 4) {
+        const int c = c0 + sl * 4;
+        const bool cact = c < a.in_c;
+        float4 s4 = make_float4(1.f, 1.f, 1.f, 1.f), b4 = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (cact && a.in_scale) s4 = *reinterpret_cast<const float4 *>(a.in_scale + c);
+        if (cact && a.in_bias) b4 = *reinterpret_cast<const float4 *>(a.in_bias + c);
+        float4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const long long pix = pix0 + (long long)u * G;
+            v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (cact && pix < a.pixels) v[u] = *reinterpret_cast<const float4 *>(a.x + pix * a.in_c + c);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const long long pix = pix0 + (long long)u * G;
+            float t[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+            if (affine) {
+                t[0] = __builtin_fmaf(t[0], s4.x, b4.x);
+                t[1] = __builtin_fmaf(t[1], s4.y, b4.y);
+                t[2] = __builtin_fmaf(t[2], s4.z, b4.z);
+                t[3] = __builtin_fmaf(t[3], s4.w, b4.w);
+            }
+            uint32_t nib = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                nib |= (t[j] < 0.0f ? 0u : 1u) << j;
+                asum[u] += fabsf(t[j]);
+            }
+            if (!cact) nib = 0;  // channels past in_c are zero bits, not signs of 0
+            if (a.bits) {
+                const uint32_t word = group_or<LPW>(nib << ((sl * 4) & 31));
+                if (cact && pix < a.pixels && (sl % LPW) == 0)
+                    a.bits[padded_pixel(a, pix) * a.words + c / 32] = word;
+            }
+        }
+    }
+    if (a.a_map) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const long long pix = pix0 + (long long)u * G;
+            const float s = group_sum<SEG>(asum[u]);
+            if (sl == 0 && pix < a.pixels) a.a_map[padded_pixel(a, pix)] = s / (float)a.in_c;
+        }
+    }
 }
 
 // One pass of a wave covers 64/SEG pixels; each pixel's channels are spread
@@ -84,14 +226,7 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a)
     const bool affine = a.in_scale != nullptr || a.in_bias != nullptr;
     const float *xp = a.x + (live ? pix : 0) * a.in_c;
 
-    long long dst = 0;
-    if (a.bits && live) {
-        const long long img = pix / ((long long)a.in_h * a.in_w);
-        const int rem = (int)(pix % ((long long)a.in_h * a.in_w));
-        const int y = rem / a.in_w, x = rem % a.in_w;
-        dst = img * a.image_words +
-              ((long long)(y + a.halo_h) * a.cols + (x + a.halo_w)) * a.words;
-    }
+    const long long dst = live ? padded_pixel(a, pix) * a.words : 0;
 
     float asum = 0.0f;
     for (int c0 = 0; c0 < a.in_c; c0 += CHUNK) {
@@ -128,41 +263,32 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a)
     if (a.a_map) {
 #pragma unroll
         for (int off = 1; off < SEG; off <<= 1) asum += __shfl_xor(asum, off, 64);
-        if (live && sl == 0) a.a_map[pix] = asum / (float)a.in_c;
+        if (live && sl == 0) a.a_map[padded_pixel(a, pix)] = asum / (float)a.in_c;
     }
 }
 
 template <int VEC, int SEG>
-hipError_t launch_pack_t(const PackArgs &a, int blocks, hipStream_t s)
+hipError_t launch_pack_t(PackArgs a, long long pack_blocks, long long halo_blocks, hipStream_t s)
 {
-    hipLaunchKernelGGL((pack_kernel<VEC, SEG>), dim3(blocks), dim3(256), 0, s, a);
+    if (pack_blocks + halo_blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    a.pack_blocks = (int)pack_blocks;
+    hipLaunchKernelGGL((pack_kernel<VEC, SEG>), dim3((unsigned)(pack_blocks + halo_blocks)), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
-// beta[i,y,x] = sum of A over the in-image taps of the window / (kh*kw).
-__global__ __launch_bounds__(256) void beta_kernel(const float *__restrict__ a_map,
-                                                   float *__restrict__ beta, int n, int in_h,
-                                                   int in_w, int out_h, int out_w, int kh, int kw,
-                                                   int sh, int sw, int ph, int pw)
+constexpr int kPackPasses = 4;  // wave passes per wave in the vec4 path
+
+template <int SEG>
+hipError_t launch_vec4_t(PackArgs a, long long halo_blocks, hipStream_t s)
 {
-    const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    const long long total = (long long)n * out_h * out_w;
-    if (t >= total) return;
-    const int ox = (int)(t % out_w);
-    const int oy = (int)((t / out_w) % out_h);
-    const long long img = t / ((long long)out_w * out_h);
-    const float *am = a_map + img * in_h * in_w;
-    float sum = 0.0f;
-    for (int ky = 0; ky < kh; ++ky) {
-        const int iy = oy * sh - ph + ky;
-        if (iy < 0 || iy >= in_h) continue;
-        for (int kx = 0; kx < kw; ++kx) {
-            const int ix = ox * sw - pw + kx;
-            if (ix < 0 || ix >= in_w) continue;
-            sum += am[(long long)iy * in_w + ix];
-        }
-    }
-    beta[t] = sum / (float)(kh * kw);
+    const long long per_wave = (64 / SEG) * kPackPasses;
+    const long long waves = (a.pixels + per_wave - 1) / per_wave;
+    const long long pack_blocks = (waves + 3) / 4;
+    if (pack_blocks + halo_blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    a.pack_blocks = (int)pack_blocks;
+    hipLaunchKernelGGL((pack_vec4<SEG, kPackPasses>), dim3((unsigned)(pack_blocks + halo_blocks)), dim3(256),
+                       0, s, a);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -190,37 +316,39 @@ hipError_t launch_pack(const Geom &g, hipStream_t s, const float *x, const float
     a.halo_pixels_per_image = (long long)g.bits_rows * g.bits_cols - (long long)g.in_h * g.in_w;
     a.halo_words = bits ? (long long)g.n * a.halo_pixels_per_image * g.words : 0;
     a.slack_words = bits ? g.bits_slack_words : 0;
+    a.halo_a = a_map ? (long long)g.n * a.halo_pixels_per_image : 0;
+    const long long halo_blocks = (a.halo_words + a.slack_words + a.halo_a + 255) / 256;
+    if (a.pixels == 0) return hipSuccess;
 
-    const int vec = (g.in_c % 4 == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0) ? 4 : 1;
+    const bool vec4 = g.in_c % 4 == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0 &&
+                      (reinterpret_cast<uintptr_t>(in_scale) & 15) == 0 &&
+                      (reinterpret_cast<uintptr_t>(in_bias) & 15) == 0;
+    const int vec = vec4 ? 4 : 1;
     int need = (g.in_c + vec - 1) / vec;
     int seg = 1;
     while (seg < need && seg < 64) seg <<= 1;
-    const long long ppw = 64 / seg;
-    const long long waves = (a.pixels + ppw - 1) / ppw;
+    if (vec4) {
+        switch (seg) {
+        case 1: return launch_vec4_t<1>(a, halo_blocks, s);
+        case 2: return launch_vec4_t<2>(a, halo_blocks, s);
+        case 4: return launch_vec4_t<4>(a, halo_blocks, s);
+        case 8: return launch_vec4_t<8>(a, halo_blocks, s);
+        case 16: return launch_vec4_t<16>(a, halo_blocks, s);
+        case 32: return launch_vec4_t<32>(a, halo_blocks, s);
+        default: return launch_vec4_t<64>(a, halo_blocks, s);
+        }
+    }
+    const long long waves = (a.pixels + (64 / seg) - 1) / (64 / seg);
     const long long pack_blocks = (waves + 3) / 4;
-    const long long halo_blocks = (a.halo_words + a.slack_words + 255) / 256;
-    if (pack_blocks + halo_blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-    a.pack_blocks = (int)pack_blocks;
-    const int blocks = (int)(pack_blocks + halo_blocks);
-    if (blocks == 0) return hipSuccess;
-#define BCONV_PACK_CASE(V, S) \
-    if (vec == V && seg == S) return launch_pack_t<V, S>(a, blocks, s);
-    BCONV_PACK_CASE(4, 1) BCONV_PACK_CASE(4, 2) BCONV_PACK_CASE(4, 4) BCONV_PACK_CASE(4, 8)
-    BCONV_PACK_CASE(4, 16) BCONV_PACK_CASE(4, 32) BCONV_PACK_CASE(4, 64)
-    BCONV_PACK_CASE(1, 1) BCONV_PACK_CASE(1, 2) BCONV_PACK_CASE(1, 4) BCONV_PACK_CASE(1, 8)
-    BCONV_PACK_CASE(1, 16) BCONV_PACK_CASE(1, 32) BCONV_PACK_CASE(1, 64)
-#undef BCONV_PACK_CASE
-    return hipErrorInvalidValue;
-}
-
-hipError_t launch_beta(const Geom &g, hipStream_t s, const float *a_map, float *beta)
-{
-    const long long total = (long long)g.n * g.out_h * g.out_w;
-    if (total == 0) return hipSuccess;
-    const long long blocks = (total + 255) / 256;
-    hipLaunchKernelGGL(beta_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a_map, beta, g.n,
-                       g.in_h, g.in_w, g.out_h, g.out_w, g.kh, g.kw, g.sh, g.sw, g.ph, g.pw);
-    return hipGetLastError();
+    switch (seg) {
+    case 1: return launch_pack_t<1, 1>(a, pack_blocks, halo_blocks, s);
+    case 2: return launch_pack_t<1, 2>(a, pack_blocks, halo_blocks, s);
+    case 4: return launch_pack_t<1, 4>(a, pack_blocks, halo_blocks, s);
+    case 8: return launch_pack_t<1, 8>(a, pack_blocks, halo_blocks, s);
+    case 16: return launch_pack_t<1, 16>(a, pack_blocks, halo_blocks, s);
+    case 32: return launch_pack_t<1, 32>(a, pack_blocks, halo_blocks, s);
+    default: return launch_pack_t<1, 64>(a, pack_blocks, halo_blocks, s);
+    }
 }
 
 }  // namespace bconv

@@ -25,7 +25,9 @@ struct XArgs {
     const uint32_t *bits;   // padded binarised input
     const uint32_t *wlane;  // [tiles][kh][kwc4][64][4]
     const int32_t *wrect;   // [tiles][(kh+1)*(kw+1)][64]
-    const float *scale, *bias, *beta;
+    const float *scale, *bias;
+    const float *a_pad;  // zero-halo A map or nullptr (beta = 1)
+    float *beta_out;
     float scale_value;
     int relu;
     float *out;
@@ -43,19 +45,21 @@ __device__ __forceinline__ void store_result(const XArgs &a, long long pix, int 
 {
     if (co >= a.out_c) return;
     const long long o = pix * a.out_c + co;
+    // Agent-scope stores write through to memory while the kernel runs, so the
+    // output does not sit dirty in L2 until the end-of-kernel write-back.
     if (a.acc_out) {
-        a.acc_out[o] = v;
+        __hip_atomic_store(&a.acc_out[o], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return;
     }
     float r = __builtin_fmaf((float)v * sc, be, bi);
     if (a.relu) r = (r < 0.0f) ? 0.0f : r;
-    a.out[o] = r;
+    __hip_atomic_store(&a.out[o], r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Specialised kernel: kernel KHxKW, CW words per pixel, horizontal stride SW,
 // P output pixels per strip.  One wave = one (strip, 64-channel tile).
 template <int KH, int KW, int CW, int SW, int P, bool AND>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void xconv_fast(XArgs a)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void xconv_fast(XArgs a)
 {
     constexpr int RW = KW * CW;            // weight words per kernel row
     constexpr int RW4 = (RW + 3) / 4;
@@ -75,6 +79,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void x
     const int ow0 = (int)(strip % (unsigned)a.strips_per_row) * P;
     const int img = (int)(row / (unsigned)a.out_h);
     const int oy = (int)(row % (unsigned)a.out_h);
+
+    // beta of pixel `lane` (lanes < P): window sum of the zero-halo A map.
+    // The loads are issued here and consumed in the epilogue.
+    float be_lane = 1.0f;
+    if (a.a_pad) {
+        float sum = 0.0f;
+        if (lane < P && ow0 + lane < a.out_w) {
+            const float *ap = a.a_pad + ((long long)img * a.rows + oy * a.sh) * a.cols + (ow0 + lane) * SW;
+#pragma unroll
+            for (int ky = 0; ky < KH; ++ky)
+#pragma unroll
+                for (int kx = 0; kx < KW; ++kx) sum += ap[ky * a.cols + kx];
+        }
+        be_lane = sum / (float)(KH * KW);
+    }
 
     uint32_t acc[P];
 #pragma unroll
@@ -122,7 +141,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void x
     const bool co_ok = co < a.out_c;
     const float sc = a.scale ? (co_ok ? a.scale[co] : 0.0f) : a.scale_value;
     const float bi = a.bias ? (co_ok ? a.bias[co] : 0.0f) : 0.0f;
-    const scalar_f32_ptr beta = (scalar_f32_ptr)a.beta;
+    if (a.a_pad && tile == 0 && lane < P && ow0 + lane < a.out_w)
+        a.beta_out[((long long)img * a.out_h + oy) * a.out_w + ow0 + lane] = be_lane;
     // In-image tap rectangle [r0, r1) x [c0, c1) of each output pixel.  Every
     // window holds at least one in-image tap because pad < kernel.
     const int iy0 = oy * a.sh - a.ph;
@@ -152,7 +172,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void x
             }
             v = a.in_c * valid - 2 * ((int)acc[p] - corr);
         }
-        const float be = a.beta ? beta[pix] : 1.0f;
+        const float be = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(be_lane), p));
         store_result(a, pix, co, v, sc, bi, be);
     }
 }
@@ -198,12 +218,20 @@ __global__ __launch_bounds__(256) void xconv_generic(XArgs a, int and_mode)
     const int v = and_mode ? (int)acc : a.in_c * valid - 2 * (int)acc;
     const float sc = a.scale ? (co_ok ? a.scale[co] : 0.0f) : a.scale_value;
     const float bi = a.bias ? (co_ok ? a.bias[co] : 0.0f) : 0.0f;
-    const float be = a.beta ? ((scalar_f32_ptr)a.beta)[pix] : 1.0f;
+    float be = 1.0f;
+    if (a.a_pad) {
+        const float *ap = a.a_pad + ((long long)img * a.rows + oy * a.sh) * a.cols + ox * a.sw;
+        float sum = 0.0f;
+        for (int ky = 0; ky < a.kh; ++ky)
+            for (int kx = 0; kx < a.kw; ++kx) sum += ap[ky * a.cols + kx];
+        be = sum / (float)(a.kh * a.kw);
+        if (tile == 0 && lane == 0) a.beta_out[pix] = be;
+    }
     store_result(a, pix, co, v, sc, bi, be);
 }
 
 template <int KH, int KW, int CW, int SW, int P>
-hipError_t launch_fast(XArgs a, hipStream_t s, int and_mode)
+hipError_t launch_fast(XArgs a, const Launch &L, int and_mode)
 {
     a.strips_per_row = (a.out_w + P - 1) / P;
     a.strips = (long long)a.n * a.out_h * a.strips_per_row;
@@ -211,16 +239,22 @@ hipError_t launch_fast(XArgs a, hipStream_t s, int and_mode)
     const long long blocks = (waves + 3) / 4;
     if (waves * 4 >= 0x7fffffffLL) return hipErrorInvalidValue;
     if (and_mode)
-        hipLaunchKernelGGL((xconv_fast<KH, KW, CW, SW, P, true>), dim3((unsigned)blocks), dim3(256), 0, s, a);
-    else
-        hipLaunchKernelGGL((xconv_fast<KH, KW, CW, SW, P, false>), dim3((unsigned)blocks), dim3(256), 0, s, a);
-    return hipGetLastError();
+        return launch_kernel(L, xconv_fast<KH, KW, CW, SW, P, true>, dim3((unsigned)blocks), dim3(256), 0, a);
+    return launch_kernel(L, xconv_fast<KH, KW, CW, SW, P, false>, dim3((unsigned)blocks), dim3(256), 0, a);
 }
 
-// Strip width: 7 when it tiles the row exactly and 8 does not, else 8.
-int strip_width(int out_w) { return (out_w % 8 != 0 && out_w % 7 == 0) ? 7 : 8; }
+// Every wave is one (strip, tile) task and all SIMDs run them at once, so
+// the kernel lasts about ceil(tasks / SIMDs) strips of P pixels plus a fixed
+// cost per strip (row loads, epilogue) of about 1.5 pixels' worth.  The strip
+// width minimises that among the compiled widths.
+double strip_cost(const Geom &g, int p)
+{
+    const long long tasks = (long long)g.n * g.out_h * ((g.out_w + p - 1) / p) * g.tiles;
+    const long long simds = g.simds > 0 ? g.simds : 1024;
+    return (double)((tasks + simds - 1) / simds) * (p + 1.5);
+}
 
-typedef hipError_t (*fast_launcher)(XArgs, hipStream_t, int);
+typedef hipError_t (*fast_launcher)(XArgs, const Launch &, int);
 
 struct FastEntry {
     int kh, kw, cw, sw, p;
@@ -231,7 +265,9 @@ struct FastEntry {
 #define BCONV_FAST(KH, KW, CW, SW, P)                                        \
     {KH, KW, CW, SW, P, &launch_fast<KH, KW, CW, SW, P>,                     \
      "xconv_fast<" #KH "," #KW "," #CW "," #SW "," #P ">"}
-#define BCONV_FAST_P(KH, KW, CW, SW) BCONV_FAST(KH, KW, CW, SW, 8), BCONV_FAST(KH, KW, CW, SW, 7)
+#define BCONV_FAST_P(KH, KW, CW, SW)                                                          \
+    BCONV_FAST(KH, KW, CW, SW, 8), BCONV_FAST(KH, KW, CW, SW, 7), BCONV_FAST(KH, KW, CW, SW, 6), \
+        BCONV_FAST(KH, KW, CW, SW, 4)
 
 const FastEntry kFast[] = {
     BCONV_FAST_P(3, 3, 1, 1), BCONV_FAST_P(3, 3, 2, 1), BCONV_FAST_P(3, 3, 3, 1),
@@ -247,12 +283,17 @@ const FastEntry kFast[] = {
 
 const FastEntry *find_fast(const Geom &g)
 {
-    // The halo must equal the padding on both axes (it does by construction)
-    // and a strip must not be wider than needed for tiny outputs.
-    const int p = strip_width(g.out_w);
-    for (const FastEntry &e : kFast)
-        if (e.kh == g.kh && e.kw == g.kw && e.cw == g.words && e.sw == g.sw && e.p == p) return &e;
-    return nullptr;
+    const FastEntry *best = nullptr;
+    double best_cost = 0.0;
+    for (const FastEntry &e : kFast) {
+        if (e.kh != g.kh || e.kw != g.kw || e.cw != g.words || e.sw != g.sw) continue;
+        const double c = strip_cost(g, e.p);
+        if (!best || c < best_cost || (c == best_cost && e.p > best->p)) {
+            best = &e;
+            best_cost = c;
+        }
+    }
+    return best;
 }
 
 XArgs make_args(const Geom &g, const uint32_t *bits, const LaneWeights &w, const Epilogue &e,
@@ -264,7 +305,8 @@ XArgs make_args(const Geom &g, const uint32_t *bits, const LaneWeights &w, const
     a.wrect = w.rect;
     a.scale = e.scale;
     a.bias = e.bias;
-    a.beta = e.beta;
+    a.a_pad = e.a_pad;
+    a.beta_out = e.beta_out;
     a.scale_value = e.scale_value;
     a.relu = e.relu;
     a.out = out;
@@ -292,8 +334,6 @@ XArgs make_args(const Geom &g, const uint32_t *bits, const LaneWeights &w, const
 
 }  // namespace
 
-int xconv_strip_width(const Geom &g) { return strip_width(g.out_w); }
-
 bool xconv_fast_available(const Geom &g) { return find_fast(g) != nullptr; }
 
 const char *xconv_kernel_name(const Geom &g)
@@ -302,19 +342,18 @@ const char *xconv_kernel_name(const Geom &g)
     return e ? e->name : "xconv_generic";
 }
 
-hipError_t launch_xconv(const Geom &g, hipStream_t s, int and_mode, const uint32_t *bits,
+hipError_t launch_xconv(const Geom &g, const Launch &L, int and_mode, const uint32_t *bits,
                         const LaneWeights &w, const Epilogue &e, float *out, int32_t *acc_out,
                         bool allow_fast)
 {
     XArgs a = make_args(g, bits, w, e, out, acc_out);
     const FastEntry *f = allow_fast ? find_fast(g) : nullptr;
-    if (f) return f->fn(a, s, and_mode);
+    if (f) return f->fn(a, L, and_mode);
     const long long waves = (long long)g.n * g.out_h * g.out_w * g.tiles;
     const long long blocks = (waves + 3) / 4;
     if (blocks == 0) return hipSuccess;
     if (waves * 4 >= 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(xconv_generic, dim3((unsigned)blocks), dim3(256), 0, s, a, and_mode);
-    return hipGetLastError();
+    return launch_kernel(L, xconv_generic, dim3((unsigned)blocks), dim3(256), 0, a, and_mode);
 }
 
 }  // namespace bconv

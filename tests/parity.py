@@ -77,8 +77,14 @@ def run_gpu(layer: workloads.Layer, inputs: dict, device, generic: bool = False)
             res["bits"] = words.reshape(n, L["bits_rows"], L["bits_cols"], L["bits_words"])
             res["bits_pad"] = (L["bits_pad_h"], L["bits_pad_w"])
         if L["a_map_offset"] is not None:
-            res["a_map"] = wsh[L["a_map_offset"]:L["a_map_offset"] + 4 * n * layer.in_h * layer.in_w] \
-                .view("<f4").reshape(n, layer.in_h, layer.in_w)
+            rows, cols = L["bits_rows"], L["bits_cols"]
+            ph, pw = L["bits_pad_h"], L["bits_pad_w"]
+            apad = wsh[L["a_map_offset"]:L["a_map_offset"] + 4 * n * rows * cols].view("<f4") \
+                .reshape(n, rows, cols)
+            res["a_map"] = apad[:, ph:ph + layer.in_h, pw:pw + layer.in_w]
+            halo = apad.copy()
+            halo[:, ph:ph + layer.in_h, pw:pw + layer.in_w] = 0
+            res["a_halo_zero"] = not halo.any()
             nb = n * conv.out_h * conv.out_w
             res["beta"] = wsh[L["beta_offset"]:L["beta_offset"] + 4 * nb].view("<f4") \
                 .reshape(n, conv.out_h, conv.out_w)
@@ -154,6 +160,7 @@ def compare(layer: workloads.Layer, inputs: dict, got: dict, ref: dict = None, i
         halo[:, ph:ph + h, pw:pw + w, :] = 0
         assert not halo.any(), f"{layer.name}: halo of the packed input is not zero"
     if layer.use_beta:
+        assert got["a_halo_zero"], f"{layer.name}: halo of the A map is not zero"
         np.testing.assert_allclose(g["a_map"], ref["a_map"], rtol=RTOL, atol=0,
                                    err_msg=f"{layer.name}: A map")
         np.testing.assert_allclose(g["beta"], ref["beta"], rtol=RTOL, atol=0,
