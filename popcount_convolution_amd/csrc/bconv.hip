@@ -24,6 +24,8 @@ struct bconv_handle {
     bconv::LaneWeights lane;  // XNOR / AND
     uint32_t *d_lane_words;
     int32_t *d_lane_popc;
+    uint32_t *d_flat;         // K-major weights of the fully connected route
+    bool gemm;
     float *d_pm;              // binaryWeights
     int pm_cols;
     float *d_out_scale, *d_out_bias, *d_in_scale, *d_in_bias;
@@ -185,7 +187,7 @@ bconv_status_t upload(const T *host, size_t count, T **dev)
 void release(bconv_handle *h)
 {
     if (!h) return;
-    void *ptrs[] = {h->d_lane_words, h->d_lane_popc, h->d_pm, h->d_out_scale,
+    void *ptrs[] = {h->d_lane_words, h->d_lane_popc, h->d_flat, h->d_pm, h->d_out_scale,
                     h->d_out_bias, h->d_in_scale, h->d_in_bias};
     for (void *p : ptrs)
         if (p) (void)hipFree(p);
@@ -248,6 +250,10 @@ bconv_status_t forward_impl(bconv_t h, void *stream, int32_t n, const float *in,
         e = bconv::launch_bwconv(g, main, in, h->d_in_scale, h->d_in_bias, h->d_pm, h->pm_cols, ep,
                                  sink == Sink::Output ? static_cast<float *>(dst) : nullptr,
                                  sink == Sink::Accum ? static_cast<float *>(dst) : nullptr);
+    } else if (h->gemm && !h->force_generic) {
+        e = bconv::launch_gemm(g, main, h->type == BCONV_AND, bits, h->d_flat, ep,
+                               sink == Sink::Output ? static_cast<float *>(dst) : nullptr,
+                               sink == Sink::Accum ? static_cast<int32_t *>(dst) : nullptr);
     } else {
         e = bconv::launch_xconv(g, main, h->type == BCONV_AND, bits, h->lane, ep,
                                 sink == Sink::Output ? static_cast<float *>(dst) : nullptr,
@@ -335,6 +341,11 @@ bconv_status_t bconv_create(const bconv_desc_t *desc, const uint32_t *weight_bit
         }
     }
     e = bconv::launch_prepack(g, nullptr, d_user, h->d_lane_words, h->d_lane_popc, h->d_pm, h->pm_cols, type);
+    h->gemm = type != BCONV_BINARY_WEIGHTS && bconv::gemm_route(g);
+    if (e == hipSuccess && h->gemm) {
+        e = hipMalloc(reinterpret_cast<void **>(&h->d_flat), bconv::gemm_weight_words(g) * 4);
+        if (e == hipSuccess) e = bconv::launch_prepack_flat(g, nullptr, d_user, h->d_flat);
+    }
     if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
     (void)hipFree(d_user);
     if (e != hipSuccess) {
@@ -419,6 +430,7 @@ const char *bconv_main_kernel(bconv_t h, int32_t n)
     const bconv::Geom g = make_geom(h, n);
     if (h->type == BCONV_BINARY_WEIGHTS) return bconv::bwconv_kernel_name(g);
     if (h->force_generic) return "xconv_generic";
+    if (h->gemm) return bconv::gemm_kernel_name(g, h->type == BCONV_AND);
     return bconv::xconv_kernel_name(g);
 }
 

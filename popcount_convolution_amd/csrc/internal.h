@@ -84,6 +84,13 @@ hipError_t launch_xconv(const Geom &g, const Launch &L, int and_mode, const uint
 // Columns of the +-1.0f binaryWeights table (out_c rounded up to the channel block).
 int bwconv_pm_cols(int out_c);
 const char *bwconv_kernel_name(const Geom &g);
+// Fully connected shape (kernel = source, stride 1, no padding): binary GEMM.
+bool gemm_route(const Geom &g);
+size_t gemm_weight_words(const Geom &g);
+hipError_t launch_prepack_flat(const Geom &g, hipStream_t s, const uint32_t *user_bits, uint32_t *flat);
+const char *gemm_kernel_name(const Geom &g, int and_mode);
+hipError_t launch_gemm(const Geom &g, const Launch &L, int and_mode, const uint32_t *bits, const uint32_t *wflat,
+                       const Epilogue &e, float *out, int32_t *acc_out);
 hipError_t launch_bwconv(const Geom &g, const Launch &L, const float *x, const float *in_scale,
                          const float *in_bias, const float *pm_weights, int pm_cols,
                          const Epilogue &e, float *out, float *acc_out);
