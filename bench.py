@@ -46,6 +46,9 @@ def parse():
     p.add_argument("--cpu-repeats", type=int, default=3)
     p.add_argument("--profile-only", action="store_true",
                    help="run warmup + timed steps and print nothing else (for rocprofv3)")
+    p.add_argument("--copy-mib", type=int, default=0,
+                   help="also run one device-to-device copy of this many MiB (calibrates HBM "
+                        "byte counters under rocprofv3 --pmc)")
     return p.parse_args()
 
 
@@ -125,6 +128,11 @@ def main():
         pca.bconv_forward_profiled(conv.handle, sptr, n, x, out, ws, ws_bytes,
                                    begins[i].cuda_event, ends[i].cuda_event)
     torch.cuda.synchronize()
+    if args.copy_mib > 0:
+        src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
     if args.profile_only:
         return
     total_ms = t0.elapsed_time(t1)

@@ -214,8 +214,10 @@ bconv_status_t forward_impl(bconv_t h, void *stream, int32_t n, const float *in,
     const size_t out_bytes = (size_t)n * h->out_h * h->out_w * d.out_c * 4;
     if (ranges_overlap(in, in_bytes, dst, out_bytes))
         return fail(BCONV_ERR_INVALID_ARGUMENT, "input and output overlap");
-    if ((long long)n * d.in_h * d.in_w >= (1LL << 31) || (long long)n * h->out_h * h->out_w * h->tiles >= (1LL << 29))
-        return fail(BCONV_ERR_INVALID_ARGUMENT, "batch too large: pixel indices must fit 31 bits");
+    if ((long long)n * d.in_h * d.in_w >= (1LL << 31) || (long long)n * h->out_h * h->out_w * h->tiles >= (1LL << 29) ||
+        in_bytes >= (size_t)0x7fffffff || out_bytes >= (size_t)0x7fffffff)
+        return fail(BCONV_ERR_INVALID_ARGUMENT,
+                    "batch too large for one call: input and output must each stay below 2 GiB");
     const bconv_workspace_layout_t L = layout_for(h, n);
     if (L.total_bytes > 0 && (!workspace || workspace_bytes < L.total_bytes))
         return fail(BCONV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total_bytes,

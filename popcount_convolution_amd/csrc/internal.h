@@ -29,6 +29,16 @@ struct Geom {
     int simds;        // SIMD units of the device (4 per compute unit)
 };
 
+// Raw buffer descriptor word 3 for gfx9-family targets (32-bit data format).
+constexpr int kBufferFlags = 0x00020000;
+// Buffer cache policy: agent-scope write-through (sc1).
+constexpr int kStoreSc1 = 16;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, int bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, bytes, kBufferFlags);
+}
+
 // Stream plus the optional hipEvents that bracket one kernel dispatch: with
 // events, the kernel is launched by hipExtLaunchKernelGGL, which records
 // them at the dispatch's own start and completion.

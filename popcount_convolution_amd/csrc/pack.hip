@@ -12,6 +12,7 @@ namespace {
 
 struct PackArgs {
     const float *x;
+    int x_bytes;            // input size in bytes (< 2^31, checked by the host)
     const float *in_scale;  // [in_c] or nullptr
     const float *in_bias;   // [in_c] or nullptr
     uint32_t *bits;         // padded bit buffer or nullptr (A only)
@@ -133,10 +134,12 @@ __device__ __forceinline__ float group_sum(float v)
 // Fast path: in_c % 4 == 0 and a 16-byte aligned input.  A pixel's channels
 // are spread over SEG lanes, four consecutive channels (one float4) per lane
 // and SEG*4 channels per chunk; a wave pass covers 64/SEG pixels and a wave
-// makes U passes over consecutive pixels with all U loads issued first.  The
+// makes U passes, so it owns a run of G*U consecutive pixels of one image
+// row, located once with scalar arithmetic (no per-lane division).  Loads and
+// stores go through buffer descriptors: a scalar base plus a lane offset.  The
 // input scale and bias of a lane's channels are loaded once per chunk.  A
-// 32-channel word is the OR of 8 lanes' 4-bit groups (DPP), |x'| is summed
-// per lane and then over the pixel's lanes in a fixed order.
+// 32-channel word is the OR of 8 lanes' 4-bit groups (DPP), |x'| is summed per
+// lane and then over the pixel's lanes in a fixed order.
 template <int SEG, int U>
 __global__ __launch_bounds__(256) void pack_vec4(PackArgs a)
 {
@@ -145,12 +148,23 @@ __global__ __launch_bounds__(256) void pack_vec4(PackArgs a)
         return;
     }
     constexpr int G = 64 / SEG;
+    constexpr int RUN = G * U;  // pixels per wave
     constexpr int LPW = SEG < 8 ? SEG : 8;
     const int lane = threadIdx.x & 63;
     const int slot = lane / SEG;
     const int sl = lane % SEG;
-    const long long wave = (long long)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-    const long long pix0 = wave * (G * U) + slot;
+    // wave -> (image row, run of RUN pixels in it); all uniform
+    const unsigned wave = blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const unsigned runs_per_row = ((unsigned)a.in_w + RUN - 1) / RUN;
+    const unsigned row_id = wave / runs_per_row;  // img * in_h + y
+    if (row_id >= (unsigned)a.n * (unsigned)a.in_h) return;
+    const int x0 = (int)(wave - row_id * runs_per_row) * RUN;
+    const unsigned img = row_id / (unsigned)a.in_h;
+    const unsigned y = row_id - img * (unsigned)a.in_h;
+    const uint32_t in_base = (row_id * (unsigned)a.in_w + (unsigned)x0) * (unsigned)a.in_c * 4u;
+    const uint32_t pad_base = ((img * (unsigned)a.rows + y + (unsigned)a.halo_h) * (unsigned)a.cols +
+                               (unsigned)(x0 + a.halo_w));  // padded pixel index of x0
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, a.x_bytes);
     const bool affine = a.in_scale != nullptr || a.in_bias != nullptr;
     float asum[U];
 #pragma unroll
@@ -164,13 +178,15 @@ __global__ __launch_bounds__(256) void pack_vec4(PackArgs a)
         float4 v[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const long long pix = pix0 + (long long)u * G;
+            const int px = x0 + u * G + slot;
             v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (cact && pix < a.pixels) v[u] = *reinterpret_cast<const float4 *>(a.x + pix * a.in_c + c);
+            if (cact && px < a.in_w)
+                v[u] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                       xr, (uint32_t)((u * G + slot) * a.in_c + c) * 4u, in_base, 0));
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const long long pix = pix0 + (long long)u * G;
+            const int px = x0 + u * G + slot;
             float t[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
             if (affine) {
                 t[0] = __builtin_fmaf(t[0], s4.x, b4.x);
@@ -187,17 +203,17 @@ __global__ __launch_bounds__(256) void pack_vec4(PackArgs a)
             if (!cact) nib = 0;  // channels past in_c are zero bits, not signs of 0
             if (a.bits) {
                 const uint32_t word = group_or<LPW>(nib << ((sl * 4) & 31));
-                if (cact && pix < a.pixels && (sl % LPW) == 0)
-                    a.bits[padded_pixel(a, pix) * a.words + c / 32] = word;
+                if (cact && px < a.in_w && (sl % LPW) == 0)
+                    a.bits[((long long)pad_base + u * G + slot) * a.words + c / 32] = word;
             }
         }
     }
     if (a.a_map) {
+        const float inv_c = 1.0f / (float)a.in_c;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const long long pix = pix0 + (long long)u * G;
             const float s = group_sum<SEG>(asum[u]);
-            if (sl == 0 && pix < a.pixels) a.a_map[padded_pixel(a, pix)] = s / (float)a.in_c;
+            if (sl == 0 && x0 + u * G + slot < a.in_w) a.a_map[(long long)pad_base + u * G + slot] = s * inv_c;
         }
     }
 }
@@ -282,7 +298,7 @@ template <int SEG>
 hipError_t launch_vec4_t(PackArgs a, long long halo_blocks, hipStream_t s)
 {
     const long long per_wave = (64 / SEG) * kPackPasses;
-    const long long waves = (a.pixels + per_wave - 1) / per_wave;
+    const long long waves = (long long)a.n * a.in_h * ((a.in_w + per_wave - 1) / per_wave);
     const long long pack_blocks = (waves + 3) / 4;
     if (pack_blocks + halo_blocks > 0x7fffffffLL) return hipErrorInvalidValue;
     a.pack_blocks = (int)pack_blocks;
@@ -298,6 +314,8 @@ hipError_t launch_pack(const Geom &g, hipStream_t s, const float *x, const float
 {
     PackArgs a{};
     a.x = x;
+    a.x_bytes = (int)((long long)g.n * g.in_h * g.in_w * g.in_c * 4 < 0x7fffffffLL
+                          ? (long long)g.n * g.in_h * g.in_w * g.in_c * 4 : 0x7fffffffLL);
     a.in_scale = in_scale;
     a.in_bias = in_bias;
     a.bits = bits;
@@ -321,6 +339,7 @@ hipError_t launch_pack(const Geom &g, hipStream_t s, const float *x, const float
     if (a.pixels == 0) return hipSuccess;
 
     const bool vec4 = g.in_c % 4 == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0 &&
+                      (long long)g.n * g.in_h * g.in_w * g.in_c * 4 < 0x7fffffffLL &&
                       (reinterpret_cast<uintptr_t>(in_scale) & 15) == 0 &&
                       (reinterpret_cast<uintptr_t>(in_bias) & 15) == 0;
     const int vec = vec4 ? 4 : 1;

@@ -38,7 +38,27 @@ struct XArgs {
     int kwc4, tiles;
     int strips_per_row;
     long long strips;
+    // buffer sizes in bytes (each < 2^31, checked by the host)
+    int out_bytes, wlane_bytes, wrect_bytes, apad_bytes, beta_bytes;
 };
+
+// Epilogue store through buffer descriptors (scalar pixel offset, lane channel
+// offset), agent-scope write-through.
+__device__ __forceinline__ void store_result_buf(const XArgs &a, const __amdgpu_buffer_rsrc_t &orr, uint32_t pix,
+                                                 int co, int v, float sc, float bi, float be)
+{
+    if (co >= a.out_c) return;
+    const uint32_t soff = pix * (uint32_t)a.out_c * 4u;
+    uint32_t bitsv;
+    if (a.acc_out) {
+        bitsv = (uint32_t)v;
+    } else {
+        float r = __builtin_fmaf((float)v * sc, be, bi);
+        if (a.relu) r = (r < 0.0f) ? 0.0f : r;
+        bitsv = __builtin_bit_cast(uint32_t, r);
+    }
+    __builtin_amdgcn_raw_buffer_store_b32(bitsv, orr, (uint32_t)(co * 4), soff, kStoreSc1);
+}
 
 __device__ __forceinline__ void store_result(const XArgs &a, long long pix, int co, int v,
                                              float sc, float bi, float be)
@@ -86,13 +106,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void x
     if (a.a_pad) {
         float sum = 0.0f;
         if (lane < P && ow0 + lane < a.out_w) {
-            const float *ap = a.a_pad + ((long long)img * a.rows + oy * a.sh) * a.cols + (ow0 + lane) * SW;
+            const __amdgpu_buffer_rsrc_t ar = make_rsrc(a.a_pad, a.apad_bytes);
+            const uint32_t abase = (uint32_t)(((img * a.rows + oy * a.sh) * a.cols + ow0 * SW) * 4);
 #pragma unroll
             for (int ky = 0; ky < KH; ++ky)
 #pragma unroll
-                for (int kx = 0; kx < KW; ++kx) sum += ap[ky * a.cols + kx];
+                for (int kx = 0; kx < KW; ++kx)
+                    sum += __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                         ar, (uint32_t)(lane * SW * 4), abase + (ky * a.cols + kx) * 4, 0));
         }
-        be_lane = sum / (float)(KH * KW);
+        be_lane = sum * (1.0f / (float)(KH * KW));
     }
 
     uint32_t acc[P];
@@ -100,7 +123,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void x
     for (int p = 0; p < P; ++p) acc[p] = 0;
 
     const scalar_u32_ptr bits = (scalar_u32_ptr)a.bits;
-    const uint4 *wl = reinterpret_cast<const uint4 *>(a.wlane) + (long long)tile * KH * RW4 * 64 + lane;
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.wlane, a.wlane_bytes);
+    const uint32_t wbase = tile * (uint32_t)(KH * RW4 * 1024);
     // Kernel rows stay a rolled loop: the strip words are invariant loads, and
     // an unrolled row loop lets the compiler hoist every row's scalar loads
     // at once, which overflows the SGPR file.  The row's weights (RW words)
@@ -110,7 +134,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void x
         uint32_t w[RW4 * 4];
 #pragma unroll
         for (int q = 0; q < RW4; ++q) {
-            const uint4 v = wl[(ky * RW4 + q) * 64];
+            const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   wr, (uint32_t)(lane * 16), wbase + (ky * RW4 + q) * 1024, 0));
             w[4 * q + 0] = v.x;
             w[4 * q + 1] = v.y;
             w[4 * q + 2] = v.z;
@@ -142,13 +167,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void x
     const float sc = a.scale ? (co_ok ? a.scale[co] : 0.0f) : a.scale_value;
     const float bi = a.bias ? (co_ok ? a.bias[co] : 0.0f) : 0.0f;
     if (a.a_pad && tile == 0 && lane < P && ow0 + lane < a.out_w)
-        a.beta_out[((long long)img * a.out_h + oy) * a.out_w + ow0 + lane] = be_lane;
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, be_lane), make_rsrc(a.beta_out, a.beta_bytes),
+                                              (uint32_t)(lane * 4), (uint32_t)(((img * a.out_h + oy) * a.out_w + ow0) * 4), 0);
     // In-image tap rectangle [r0, r1) x [c0, c1) of each output pixel.  Every
     // window holds at least one in-image tap because pad < kernel.
+    const __amdgpu_buffer_rsrc_t orr = make_rsrc(a.acc_out ? (const void *)a.acc_out : (const void *)a.out, a.out_bytes);
     const int iy0 = oy * a.sh - a.ph;
     const int r0 = iy0 < 0 ? -iy0 : 0;
     const int r1 = a.in_h - iy0 < KH ? a.in_h - iy0 : KH;
-    const int32_t *rect = a.wrect + (long long)tile * (KH + 1) * (KW + 1) * 64 + lane;
+    const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.wrect, a.wrect_bytes);
+    const uint32_t rbase = tile * (uint32_t)((KH + 1) * (KW + 1) * 256);
+    auto rect = [&](int e) {
+        return (int)__builtin_amdgcn_raw_buffer_load_b32(rr, (uint32_t)(lane * 4), rbase + e * 256, 0);
+    };
 #pragma unroll
     for (int p = 0; p < P; ++p) {
         const int ox = ow0 + p;
@@ -165,15 +196,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void x
             int corr = 0;
             if (valid != KH * KW) {
                 // set weight bits at padded taps = total - in-image rectangle
-                const int total = rect[(KH * (KW + 1) + KW) * 64];
-                const int inside = rect[(r1 * (KW + 1) + c1) * 64] - rect[(r0 * (KW + 1) + c1) * 64] -
-                                   rect[(r1 * (KW + 1) + c0) * 64] + rect[(r0 * (KW + 1) + c0) * 64];
+                const int total = rect(KH * (KW + 1) + KW);
+                const int inside = rect(r1 * (KW + 1) + c1) - rect(r0 * (KW + 1) + c1) -
+                                   rect(r1 * (KW + 1) + c0) + rect(r0 * (KW + 1) + c0);
                 corr = total - inside;
             }
             v = a.in_c * valid - 2 * ((int)acc[p] - corr);
         }
         const float be = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(be_lane), p));
-        store_result(a, pix, co, v, sc, bi, be);
+        store_result_buf(a, orr, (uint32_t)pix, co, v, sc, bi, be);
     }
 }
 
@@ -329,6 +360,11 @@ XArgs make_args(const Geom &g, const uint32_t *bits, const LaneWeights &w, const
     a.cols = g.bits_cols;
     a.kwc4 = w.kwc4;
     a.tiles = g.tiles;
+    a.out_bytes = (int)((long long)g.n * g.out_h * g.out_w * g.out_c * 4);
+    a.wlane_bytes = (int)((long long)g.tiles * g.kh * w.kwc4 * 1024);
+    a.wrect_bytes = (int)((long long)g.tiles * (g.kh + 1) * (g.kw + 1) * 256);
+    a.apad_bytes = (int)((long long)g.n * g.bits_rows * g.bits_cols * 4);
+    a.beta_bytes = (int)((long long)g.n * g.out_h * g.out_w * 4);
     return a;
 }
 
