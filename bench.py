@@ -6,10 +6,11 @@ epilogue) over one batch of the measured layer, inputs already resident in
 HBM.  Prints one JSON line:
   value      nominal bit-MACs (N*Ho*Wo*Cout*kh*kw*Cin) per second of whole
              steps, in G bit-MAC/s (= binary GOPS);
-  roofline   the convolution kernel alone: its bit-MACs per launch over its
-             average duration, from hipEvents that the convolution dispatch
-             records itself (a second pass over the same K steps, so the
-             events do not perturb `value`), against the VALU popcount peak;
+  roofline   the convolution kernel alone, timed by hipEvents that its
+             dispatch records itself (a second pass over the same K steps, so
+             the events do not perturb `value`), against whichever peak binds
+             it: the VALU popcount peak (XNOR/AND), the bf16 matrix cores at
+             three products per fp32 product (binaryWeights), or HBM;
   cpu_baseline  the CPU oracle timed on a bounded sample of the same layer.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layer I]
@@ -31,8 +32,29 @@ if ROOT not in sys.path:
 # XNOR/AND cost 2 lane-ops (xor/and, then bcnt with accumulate) per 32 bit-MACs.
 VALU_LANE_OPS = 256 * 64 * 2.4e9
 POPCOUNT_PEAK_TBITMAC = VALU_LANE_OPS * 16 / 1e12          # 629.1
-# binaryWeights: one fp32 FMA per MAC on the VALU (packed forms not used).
-FP32_FMA_PEAK_TMAC = VALU_LANE_OPS / 1e12                  # 39.3
+# binaryWeights runs on the bf16 matrix cores (2.5 PFLOP/s dense), three bf16
+# products per exact fp32 product: 2500/3 TFLOP/s of fp32-exact work.
+BF16X3_PEAK_TFLOPS = 2500.0 / 3
+HBM_PEAK_GBS = 8000.0
+
+
+def algorithmic_bytes(layer, n):
+    """Bytes the convolution / matrix kernel must move at least: its input
+    operand once (packed bits for XNOR/AND, fp32 for binaryWeights), the A
+    map when beta is on, the weight bits and the fp32 output."""
+    words = (layer.in_c + 31) // 32
+    if layer.is_fc:
+        rows, cols = layer.in_h, layer.in_w
+    else:
+        rows, cols = layer.in_h + 2 * layer.pad_h, layer.in_w + 2 * layer.pad_w
+    if layer.type == "binary_weights":
+        src = n * layer.in_h * layer.in_w * layer.in_c * 4
+    else:
+        src = n * rows * cols * words * 4
+    amap = n * rows * cols * 4 if layer.use_beta else 0
+    weights = layer.out_c * layer.kernel_h * layer.kernel_w * words * 4
+    out = n * layer.out_h * layer.out_w * layer.out_c * 4
+    return src + amap + weights + out
 
 
 def parse():
@@ -141,8 +163,19 @@ def main():
     macs = layer.nominal_macs()
     value = macs / (ms_per_step / 1e3) / 1e9
     binary = layer.type != "binary_weights"
-    achieved = macs / (main_ms / 1e3) / 1e12
-    peak = POPCOUNT_PEAK_TBITMAC if binary else FP32_FMA_PEAK_TMAC
+    # the roofline is whichever of compute and HBM takes longer at peak
+    nbytes = algorithmic_bytes(layer, n)
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+    if binary:
+        t_cmp = macs / (POPCOUNT_PEAK_TBITMAC * 1e12)
+        cmp = ("alu", macs / (main_ms / 1e3) / 1e12, POPCOUNT_PEAK_TBITMAC, "Tbit-MAC/s")
+    else:
+        t_cmp = 2 * macs / (BF16X3_PEAK_TFLOPS * 1e12)
+        cmp = ("mfma", 2 * macs / (main_ms / 1e3) / 1e12, BF16X3_PEAK_TFLOPS, "TFLOP/s (fp32-exact, bf16x3)")
+    if t_hbm > t_cmp:
+        bound, achieved, peak, runit = "hbm", nbytes / (main_ms / 1e3) / 1e9, HBM_PEAK_GBS, "GB/s"
+    else:
+        bound, achieved, peak, runit = cmp
     traffic = None
     tfile = os.path.join(ROOT, "profiles", "traffic.json")
     kernel = conv.main_kernel(n)
@@ -171,10 +204,10 @@ def main():
                    "stride": [layer.stride_h, layer.stride_w], "pad": [layer.pad_h, layer.pad_w],
                    "beta": layer.use_beta, "input_affine": layer.iscale_dist is not None,
                    "neuron": layer.neuron, "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "alu", "kernel": kernel, "achieved": round(achieved, 3),
-                     "peak": round(peak, 3),
-                     "unit": "Tbit-MAC/s" if binary else "TMAC/s (fp32 FMA)",
+        "roofline": {"bound": bound, "kernel": kernel, "achieved": round(achieved, 3),
+                     "peak": round(peak, 3), "unit": runit,
                      "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "algorithmic_bytes": nbytes,
                      "avg_kernel_us": round(main_ms * 1e3, 3)},
     }
     if args.cpu_images > 0:

@@ -9,6 +9,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "bconv.h"
 #include "internal.h"
@@ -26,8 +27,9 @@ struct bconv_handle {
     int32_t *d_lane_popc;
     uint32_t *d_flat;         // K-major weights of the fully connected route
     bool gemm;
-    float *d_pm;              // binaryWeights
+    float *d_pm;              // binaryWeights, VALU kernel (+-1.0f table)
     int pm_cols;
+    void *d_mma;              // binaryWeights, matrix-core kernel (bf16 fragments)
     float *d_out_scale, *d_out_bias, *d_in_scale, *d_in_bias;
 };
 
@@ -187,7 +189,7 @@ bconv_status_t upload(const T *host, size_t count, T **dev)
 void release(bconv_handle *h)
 {
     if (!h) return;
-    void *ptrs[] = {h->d_lane_words, h->d_lane_popc, h->d_flat, h->d_pm, h->d_out_scale,
+    void *ptrs[] = {h->d_lane_words, h->d_lane_popc, h->d_flat, h->d_pm, h->d_mma, h->d_out_scale,
                     h->d_out_bias, h->d_in_scale, h->d_in_bias};
     for (void *p : ptrs)
         if (p) (void)hipFree(p);
@@ -248,7 +250,11 @@ bconv_status_t forward_impl(bconv_t h, void *stream, int32_t n, const float *in,
     ep.beta_out = beta;
     ep.relu = d.neuron == BCONV_NEURON_RELU;
     const bconv::Launch main{s, static_cast<hipEvent_t>(ev_begin), static_cast<hipEvent_t>(ev_end)};
-    if (h->type == BCONV_BINARY_WEIGHTS) {
+    if (h->type == BCONV_BINARY_WEIGHTS && !h->force_generic) {
+        e = bconv::launch_bwmma(g, main, in, h->d_in_scale, h->d_in_bias, h->d_mma, ep,
+                                sink == Sink::Output ? static_cast<float *>(dst) : nullptr,
+                                sink == Sink::Accum ? static_cast<float *>(dst) : nullptr);
+    } else if (h->type == BCONV_BINARY_WEIGHTS) {
         e = bconv::launch_bwconv(g, main, in, h->d_in_scale, h->d_in_bias, h->d_pm, h->pm_cols, ep,
                                  sink == Sink::Output ? static_cast<float *>(dst) : nullptr,
                                  sink == Sink::Accum ? static_cast<float *>(dst) : nullptr);
@@ -318,6 +324,16 @@ bconv_status_t bconv_create(const bconv_desc_t *desc, const uint32_t *weight_bit
         release(h);
         return st;
     }
+    // An input affine is held as both arrays: a missing scale is 1, a missing bias 0.
+    if ((h->d_in_scale == nullptr) != (h->d_in_bias == nullptr)) {
+        const std::vector<float> identity((size_t)desc->in_c, h->d_in_scale ? 0.0f : 1.0f);
+        st = upload(identity.data(), identity.size(), h->d_in_scale ? &h->d_in_bias : &h->d_in_scale);
+        if (st != BCONV_OK) {
+            (void)hipFree(d_user);
+            release(h);
+            return st;
+        }
+    }
 
     const bconv::Geom g = make_geom(h, 1);
     if (type != BCONV_BINARY_WEIGHTS) {
@@ -336,6 +352,7 @@ bconv_status_t bconv_create(const bconv_desc_t *desc, const uint32_t *weight_bit
     } else {
         h->pm_cols = bconv::bwconv_pm_cols(desc->out_c);
         e = hipMalloc(reinterpret_cast<void **>(&h->d_pm), (size_t)taps * desc->in_c * h->pm_cols * 4);
+        if (e == hipSuccess) e = hipMalloc(&h->d_mma, bconv::bwmma_frag_bytes(g));
         if (e != hipSuccess) {
             (void)hipFree(d_user);
             release(h);
@@ -343,6 +360,7 @@ bconv_status_t bconv_create(const bconv_desc_t *desc, const uint32_t *weight_bit
         }
     }
     e = bconv::launch_prepack(g, nullptr, d_user, h->d_lane_words, h->d_lane_popc, h->d_pm, h->pm_cols, type);
+    if (e == hipSuccess && type == BCONV_BINARY_WEIGHTS) e = bconv::launch_prepack_bwmma(g, nullptr, d_user, h->d_mma);
     h->gemm = type != BCONV_BINARY_WEIGHTS && bconv::gemm_route(g);
     if (e == hipSuccess && h->gemm) {
         e = hipMalloc(reinterpret_cast<void **>(&h->d_flat), bconv::gemm_weight_words(g) * 4);
@@ -430,7 +448,8 @@ const char *bconv_main_kernel(bconv_t h, int32_t n)
 {
     if (!h || n < 0) return "";
     const bconv::Geom g = make_geom(h, n);
-    if (h->type == BCONV_BINARY_WEIGHTS) return bconv::bwconv_kernel_name(g);
+    if (h->type == BCONV_BINARY_WEIGHTS)
+        return h->force_generic ? bconv::bwconv_kernel_name(g) : bconv::bwmma_kernel_name(g, h->d_in_scale != nullptr);
     if (h->force_generic) return "xconv_generic";
     if (h->gemm) return bconv::gemm_kernel_name(g, h->type == BCONV_AND);
     return bconv::xconv_kernel_name(g);

@@ -105,4 +105,12 @@ hipError_t launch_bwconv(const Geom &g, const Launch &L, const float *x, const f
                          const float *in_bias, const float *pm_weights, int pm_cols,
                          const Epilogue &e, float *out, float *acc_out);
 
+// binaryWeights on the bf16 matrix cores (exact three-way split of the input).
+size_t bwmma_frag_bytes(const Geom &g);
+hipError_t launch_prepack_bwmma(const Geom &g, hipStream_t s, const uint32_t *user_bits, void *frag);
+// `affine`: the layer has an input scale/bias (then both device arrays exist).
+const char *bwmma_kernel_name(const Geom &g, bool affine);
+hipError_t launch_bwmma(const Geom &g, const Launch &L, const float *x, const float *in_scale, const float *in_bias,
+                        const void *frag, const Epilogue &e, float *out, float *acc_out);
+
 }  // namespace bconv

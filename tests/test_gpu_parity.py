@@ -123,9 +123,8 @@ def test_sweep(dev, layer):
     ref = oracle.bconv_layer(layer, inputs)
     got = parity.run_gpu(layer, inputs, dev)
     parity.compare(layer, inputs, got, ref=ref)
-    if layer.type != "binary_weights":
-        gen = parity.run_gpu(layer, inputs, dev, generic=True)
-        parity.compare(layer, inputs, gen, ref=ref)
+    gen = parity.run_gpu(layer, inputs, dev, generic=True)
+    parity.compare(layer, inputs, gen, ref=ref)
 
 
 def test_special_values(dev):
@@ -146,6 +145,41 @@ def test_special_values(dev):
         assert np.array_equal(got["acc"], ref["acc"])
         ph, pw = got["bits_pad"]
         assert np.array_equal(got["bits"][:, ph:ph + 4, pw:pw + 4], parity.expected_words(ref["signs"], form))
+
+
+def test_binary_weights_special_values(dev):
+    """binaryWeights keeps full-precision input: infinities and NaN propagate
+    as in the oracle's sum (same sign of infinity, NaN where it has NaN),
+    signed zeros and subnormals count at their value, and an image of tiny
+    values (whose low-order pieces are subnormal) meets the normwise bound
+    with no absolute slack.  Both kernels (matrix-core and VALU)."""
+    layer = workloads.Layer("special_bw", "binary_weights", 3, 6, 7, 64, 70, 3, 3, 1, 1, 1, 1)
+    inputs = workloads.make_inputs(layer, 92)
+    x = inputs["x"]
+    specials = np.array([0.0, -0.0, 1e-40, -1e-40, 1e-45, -1e-45, np.inf, -np.inf, np.nan],
+                        np.float32)
+    img0 = x[0].reshape(-1)
+    img0[: specials.size * 97: 97] = specials
+    x[1] = x[1] * np.float32(1e-37)       # normal fp32, pieces below bf16's normal range
+    x[2] = x[2] * np.float32(1e-41)       # subnormal fp32
+    inputs["x"] = x
+    ref = oracle.bconv_layer(layer, inputs)
+    S = parity.window_abs_sum(layer, inputs)[..., None]
+    for generic in (False, True):
+        got = parity.run_gpu(layer, inputs, dev, generic=generic)
+        for key in ("acc", "out"):
+            g, o = got[key].astype(np.float64), ref[key]
+            nonfinite = ~np.isfinite(o)
+            assert nonfinite[0].any(), "the specials must reach some window"
+            assert np.array_equal(np.isnan(g), np.isnan(o)), f"{key}: NaN positions differ"
+            inf = np.isinf(o)
+            assert np.array_equal(g[inf], o[inf]), f"{key}: infinities differ"
+        g, o = got["acc"].astype(np.float64), ref["acc"]
+        fin = np.isfinite(o) & np.isfinite(S)
+        err = np.abs(g - o)
+        assert np.all(err[fin] <= parity.RTOL * np.broadcast_to(S, o.shape)[fin]), \
+            f"generic={generic}: sums off by {err[fin].max()}"
+        assert np.any(g[1] != 0) and np.any(g[2] != 0), "tiny values must not flush to zero"
 
 
 # ------------------------------------------------------------ robustness
