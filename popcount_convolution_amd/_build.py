@@ -48,7 +48,12 @@ def _compile(src: str) -> str:
 
 
 def build(jobs: int = 8) -> str:
-    """Compile every HIP source and link libbconv.so; returns its path."""
+    """Compile every HIP source and link libbconv.so; returns its path.
+
+    The previous library is removed first, so a failed build leaves none
+    behind (callers then fail loudly instead of loading stale kernels)."""
+    if os.path.exists(LIB):
+        os.remove(LIB)
     os.makedirs(BUILD, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(SOURCES)))) as ex:
         objs = list(ex.map(_compile, SOURCES))

@@ -339,7 +339,7 @@ bconv_status_t bconv_create(const bconv_desc_t *desc, const uint32_t *weight_bit
     if (type != BCONV_BINARY_WEIGHTS) {
         h->lane.kwc4 = (desc->kernel_w * h->words + 3) / 4;
         const size_t nw = (size_t)h->tiles * desc->kernel_h * h->lane.kwc4 * 256;
-        const size_t np = (size_t)h->tiles * (desc->kernel_h + 1) * (desc->kernel_w + 1) * 64;
+        const size_t np = (size_t)h->tiles * (desc->kernel_h + 1) * bconv::rect_row(desc->kernel_w) * 64;
         e = hipMalloc(reinterpret_cast<void **>(&h->d_lane_words), nw * 4);
         if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&h->d_lane_popc), np * 4);
         if (e != hipSuccess) {

@@ -64,9 +64,35 @@ hipError_t launch_kernel(const Launch &L, F kernel, dim3 grid, dim3 block, uint3
 // >= in_c are cleared.
 struct LaneWeights {
     const uint32_t *words;  // device
-    const int32_t *rect;    // [tiles][(kh+1)*(kw+1)][64]: prefix sums of tap popcounts
+    const int32_t *rect;    // [tiles][64][(kh+1)*rect_row]: prefix sums of tap popcounts
     int kwc4;
 };
+
+// Entries per row of a lane's prefix-sum table: kw+1 rounded up to a multiple
+// of 4, so each table row is whole 16-byte loads.
+__host__ __device__ inline int rect_row(int kw) { return (kw + 1 + 3) / 4 * 4; }
+
+// Unsigned division by a runtime divisor d (1 <= d < 2^31) of numerators
+// n < 2^31 as a multiply-high and a shift: with l = ceil(log2 d) >= 1,
+// m = floor(2^(31+l) / d) + 1 fits 32 bits and n/d = mulhi(n, m) >> (l-1)
+// (the error term n*(m*d - 2^(31+l)) / (d*2^(31+l)) stays below 1/d).  d = 1
+// is m = 0: the quotient is n.
+struct FastDiv {
+    uint32_t m;
+    int s;
+};
+inline FastDiv make_fastdiv(uint32_t d)
+{
+    if (d <= 1) return FastDiv{0u, 0};
+    int l = 0;
+    while ((1ull << l) < d) ++l;
+    const unsigned long long m = (1ull << (31 + l)) / d + 1;
+    return FastDiv{(uint32_t)m, l - 1};
+}
+__device__ __forceinline__ uint32_t fastdiv(uint32_t n, FastDiv f)
+{
+    return f.m ? (__umulhi(n, f.m) >> f.s) : n;
+}
 
 // Epilogue operands.  With a_pad set, the convolution kernels form beta as
 // the window sum of the zero-halo A map / (kh*kw) and also store it to

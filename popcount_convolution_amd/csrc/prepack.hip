@@ -9,8 +9,9 @@
 //     so a wave loads 256 contiguous bytes per 4 words; bits >= in_c are
 //     cleared, padding channels and r >= kw*words are 0;
 //   * a per-lane 2-D prefix sum of the tap popcounts,
-//     rect[tiles][(kh+1)*(kw+1)][64], rect[a][b] = set bits of the cleared
-//     words of taps ky < a, kx < b.  It serves the XNOR border correction: a
+//     rect[tiles][64][(kh+1)*R] (R = kw+1 rounded up to 4, padding 0),
+//     entry a*R + b = set bits of the cleared words of taps ky < a, kx < b;
+//     lane-major so a lane reads a table row with whole 16-byte loads.  It serves the XNOR border correction: a
 //     zero input word at a padded tap counts every set weight bit as a
 //     disagreement, and those bits are total - (in-image rectangle);
 //   * binaryWeights: +-1.0f [kh*kw*in_c][pm_cols] (zero for channels >=
@@ -36,7 +37,8 @@ __global__ void prepack_lane_kernel(const uint32_t *__restrict__ user, uint32_t 
     const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     const int taps = kh * kw;
     const long long n_words = (long long)tiles * kh * kwc4 * 64 * 4;
-    const int rect = (kh + 1) * (kw + 1);
+    const int rrow = rect_row(kw);
+    const int rect = (kh + 1) * rrow;
     const long long n_popc = (long long)tiles * rect * 64;
     if (t < n_words) {
         const int j = (int)(t % 4);
@@ -52,13 +54,13 @@ __global__ void prepack_lane_kernel(const uint32_t *__restrict__ user, uint32_t 
         lane_words[t] = v;
     } else if (t < n_words + n_popc) {
         const long long u = t - n_words;
-        const int lane = (int)(u % 64);
-        const int e = (int)((u / 64) % rect);
+        const int e = (int)(u % rect);
+        const int lane = (int)((u / rect) % 64);
         const int tile = (int)(u / (64LL * rect));
-        const int ra = e / (kw + 1), rb = e % (kw + 1);
+        const int ra = e / rrow, rb = e % rrow;
         const int co = tile * kTile + lane;
         int pc = 0;
-        if (co < out_c)
+        if (co < out_c && rb <= kw)
             for (int ky = 0; ky < ra; ++ky)
                 for (int kx = 0; kx < rb; ++kx)
                     for (int w = 0; w < words; ++w)
@@ -94,7 +96,7 @@ hipError_t launch_prepack(const Geom &g, hipStream_t s, const uint32_t *user_bit
     if (type != BCONV_BINARY_WEIGHTS) {
         const int kwc4 = (g.kw * g.words + 3) / 4;
         const long long total = (long long)g.tiles * g.kh * kwc4 * 256 +
-                                (long long)g.tiles * (g.kh + 1) * (g.kw + 1) * 64;
+                                (long long)g.tiles * (g.kh + 1) * rect_row(g.kw) * 64;
         hipLaunchKernelGGL(prepack_lane_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
                            user_bits, lane_words, lane_popc, g.out_c, g.kh, g.kw, g.words, g.in_c,
                            g.tiles, kwc4);

@@ -24,7 +24,7 @@ typedef const float __attribute__((address_space(4))) *scalar_f32_ptr;
 struct XArgs {
     const uint32_t *bits;   // padded binarised input
     const uint32_t *wlane;  // [tiles][kh][kwc4][64][4]
-    const int32_t *wrect;   // [tiles][(kh+1)*(kw+1)][64]
+    const int32_t *wrect;   // [tiles][64][(kh+1)*rect_row(kw)]
     const float *scale, *bias;
     const float *a_pad;  // zero-halo A map or nullptr (beta = 1)
     float *beta_out;
@@ -38,17 +38,20 @@ struct XArgs {
     int kwc4, tiles;
     int strips_per_row;
     long long strips;
+    FastDiv div_tiles, div_spr, div_oh;  // by tiles, strips_per_row, out_h
     // buffer sizes in bytes (each < 2^31, checked by the host)
     int out_bytes, wlane_bytes, wrect_bytes, apad_bytes, beta_bytes;
 };
 
 // Epilogue store through buffer descriptors (scalar pixel offset, lane channel
 // offset), agent-scope write-through.
-__device__ __forceinline__ void store_result_buf(const XArgs &a, const __amdgpu_buffer_rsrc_t &orr, uint32_t pix,
+// `soff` (the pixel's byte offset) must be wave-uniform; it is forced into an
+// SGPR so the store takes it as its scalar offset.
+__device__ __forceinline__ void store_result_buf(const XArgs &a, const __amdgpu_buffer_rsrc_t &orr, uint32_t soff,
                                                  int co, int v, float sc, float bi, float be)
 {
     if (co >= a.out_c) return;
-    const uint32_t soff = pix * (uint32_t)a.out_c * 4u;
+    soff = __builtin_amdgcn_readfirstlane(soff);
     uint32_t bitsv;
     if (a.acc_out) {
         bitsv = (uint32_t)v;
@@ -91,31 +94,95 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void x
     // Work indices fit 31 bits (the host checks strips * tiles < 2^31).
     const int lane = threadIdx.x & 63;
     const unsigned gw = blockIdx.x * 4u + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const unsigned tile = gw % (unsigned)a.tiles;
-    const unsigned strip = gw / (unsigned)a.tiles;
+    // (scalar multiply-high divisions by host-computed reciprocals)
+    const unsigned strip = fastdiv(gw, a.div_tiles);
+    const unsigned tile = gw - strip * (unsigned)a.tiles;
     if (strip >= (unsigned)a.strips) return;
 
-    const unsigned row = strip / (unsigned)a.strips_per_row;
-    const int ow0 = (int)(strip % (unsigned)a.strips_per_row) * P;
-    const int img = (int)(row / (unsigned)a.out_h);
-    const int oy = (int)(row % (unsigned)a.out_h);
+    const unsigned row = fastdiv(strip, a.div_spr);
+    const int ow0 = (int)(strip - row * (unsigned)a.strips_per_row) * P;
+    const unsigned imgu = fastdiv(row, a.div_oh);
+    const int img = (int)imgu;
+    const int oy = (int)(row - imgu * (unsigned)a.out_h);
 
     // beta of pixel `lane` (lanes < P): window sum of the zero-halo A map.
-    // The loads are issued here and consumed in the epilogue.
+    // One load brings the strip's KH x NCOL patch (row r in lanes 16r..16r+15);
+    // cross-lane sums then add each window.  Consumed in the epilogue.
     float be_lane = 1.0f;
     if (a.a_pad) {
-        float sum = 0.0f;
-        if (lane < P && ow0 + lane < a.out_w) {
-            const __amdgpu_buffer_rsrc_t ar = make_rsrc(a.a_pad, a.apad_bytes);
-            const uint32_t abase = (uint32_t)(((img * a.rows + oy * a.sh) * a.cols + ow0 * SW) * 4);
+        const __amdgpu_buffer_rsrc_t ar = make_rsrc(a.a_pad, a.apad_bytes);
+        const uint32_t abase = (uint32_t)(((img * a.rows + oy * a.sh) * a.cols + ow0 * SW) * 4);
+        if constexpr (KH <= 4 && NCOL <= 16) {
+            const int pr = lane >> 4, pc = lane & 15;
+            // the patch stays inside the zero-halo map except past the last
+            // column of a ragged strip: those read zero (buffer range) or a
+            // neighbouring pixel's value, and feed only pixels that are not stored
+            const bool in_patch = pr < KH && pc < NCOL;
+            const float v = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                          ar, in_patch ? (uint32_t)((pr * a.cols + pc) * 4) : 0x80000000u, abase, 0));
+            float colsum = v;
 #pragma unroll
-            for (int ky = 0; ky < KH; ++ky)
+            for (int r = 1; r < KH; ++r) colsum += __shfl(v, (lane + 16 * r) & 63);
+            float sum = 0.0f;
 #pragma unroll
-                for (int kx = 0; kx < KW; ++kx)
-                    sum += __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                         ar, (uint32_t)(lane * SW * 4), abase + (ky * a.cols + kx) * 4, 0));
+            for (int kx = 0; kx < KW; ++kx) sum += __shfl(colsum, (lane * SW + kx) & 63);
+            be_lane = sum * (1.0f / (float)(KH * KW));
+        } else {
+            float sum = 0.0f;
+            if (lane < P && ow0 + lane < a.out_w) {
+#pragma unroll
+                for (int ky = 0; ky < KH; ++ky)
+#pragma unroll
+                    for (int kx = 0; kx < KW; ++kx)
+                        sum += __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                             ar, (uint32_t)(lane * SW * 4), abase + (ky * a.cols + kx) * 4, 0));
+            }
+            be_lane = sum * (1.0f / (float)(KH * KW));
         }
-        be_lane = sum * (1.0f / (float)(KH * KW));
+    }
+
+    // Epilogue operands are loaded here, so their latency overlaps the first
+    // kernel row's loads instead of sitting at the end of the wave.
+    const int co = tile * kTile + lane;
+    const bool co_ok = co < a.out_c;
+    const float sc = a.scale ? (co_ok ? a.scale[co] : 0.0f) : a.scale_value;
+    const float bi = a.bias ? (co_ok ? a.bias[co] : 0.0f) : 0.0f;
+    // In-image tap rows [r0, r1) of this strip; every window holds at least
+    // one in-image tap because pad < kernel.
+    const int iy0 = oy * a.sh - a.ph;
+    const int r0 = iy0 < 0 ? -iy0 : 0;
+    const int r1 = a.in_h - iy0 < KH ? a.in_h - iy0 : KH;
+    // XNOR border correction: a zero input word at a padded tap counts every
+    // set weight bit as a disagreement; those bits are total - (in-image
+    // rectangle), from the lane's prefix sums rect[a][b] (taps ky < a, kx < b).
+    // A strip needs rows r0 and r1 of the table and the total.
+    int rt0[KW + 1], rt1[KW + 1], rtotal = 0;
+#pragma unroll
+    for (int c = 0; c <= KW; ++c) rt0[c] = rt1[c] = 0;
+    const int ixa = ow0 * SW - a.pw;                 // first pixel's first tap column
+    const int ixz = (ow0 + P - 1) * SW - a.pw + KW;  // one past the last pixel's last tap
+    const bool border = r0 > 0 || r1 < KH || ixa < 0 || ixz > a.in_w;
+    if (!AND && border) {
+        // lane-major table: this lane's rows r0, r1 and KH are whole 16-byte loads
+        constexpr int RR = (KW + 1 + 3) / 4 * 4;
+        const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.wrect, a.wrect_bytes);
+        const uint32_t lbase = (uint32_t)((tile * 64 + lane) * (KH + 1) * RR) * 4u;
+        int t0[RR], t1[RR], tk[RR];
+#pragma unroll
+        for (int q = 0; q < RR / 4; ++q) {
+            const uint4 v0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rr, lbase, (r0 * RR + 4 * q) * 4, 0));
+            const uint4 v1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rr, lbase, (r1 * RR + 4 * q) * 4, 0));
+            const uint4 vk = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rr, lbase, (KH * RR + 4 * q) * 4, 0));
+            t0[4 * q] = (int)v0.x; t0[4 * q + 1] = (int)v0.y; t0[4 * q + 2] = (int)v0.z; t0[4 * q + 3] = (int)v0.w;
+            t1[4 * q] = (int)v1.x; t1[4 * q + 1] = (int)v1.y; t1[4 * q + 2] = (int)v1.z; t1[4 * q + 3] = (int)v1.w;
+            tk[4 * q] = (int)vk.x; tk[4 * q + 1] = (int)vk.y; tk[4 * q + 2] = (int)vk.z; tk[4 * q + 3] = (int)vk.w;
+        }
+#pragma unroll
+        for (int c = 0; c <= KW; ++c) {
+            rt0[c] = t0[c];
+            rt1[c] = t1[c];
+        }
+        rtotal = tk[KW];
     }
 
     uint32_t acc[P];
@@ -162,29 +229,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void x
         }
     }
 
-    const int co = tile * kTile + lane;
-    const bool co_ok = co < a.out_c;
-    const float sc = a.scale ? (co_ok ? a.scale[co] : 0.0f) : a.scale_value;
-    const float bi = a.bias ? (co_ok ? a.bias[co] : 0.0f) : 0.0f;
     if (a.a_pad && tile == 0 && lane < P && ow0 + lane < a.out_w)
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, be_lane), make_rsrc(a.beta_out, a.beta_bytes),
                                               (uint32_t)(lane * 4), (uint32_t)(((img * a.out_h + oy) * a.out_w + ow0) * 4), 0);
-    // In-image tap rectangle [r0, r1) x [c0, c1) of each output pixel.  Every
-    // window holds at least one in-image tap because pad < kernel.
     const __amdgpu_buffer_rsrc_t orr = make_rsrc(a.acc_out ? (const void *)a.acc_out : (const void *)a.out, a.out_bytes);
-    const int iy0 = oy * a.sh - a.ph;
-    const int r0 = iy0 < 0 ? -iy0 : 0;
-    const int r1 = a.in_h - iy0 < KH ? a.in_h - iy0 : KH;
-    const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.wrect, a.wrect_bytes);
-    const uint32_t rbase = tile * (uint32_t)((KH + 1) * (KW + 1) * 256);
-    auto rect = [&](int e) {
-        return (int)__builtin_amdgcn_raw_buffer_load_b32(rr, (uint32_t)(lane * 4), rbase + e * 256, 0);
-    };
+    // byte offset of the strip's first output pixel, and the stride between pixels
+    const uint32_t obase =
+        __builtin_amdgcn_readfirstlane((uint32_t)(((img * a.out_h + oy) * a.out_w + ow0) * a.out_c) * 4u);
+    const uint32_t ostep = (uint32_t)a.out_c * 4u;
 #pragma unroll
     for (int p = 0; p < P; ++p) {
         const int ox = ow0 + p;
         if (ox >= a.out_w) break;
-        const long long pix = ((long long)img * a.out_h + oy) * a.out_w + ox;
         int v;
         if (AND) {
             v = (int)acc[p];  // a zero word at a padded tap adds nothing
@@ -196,15 +252,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void x
             int corr = 0;
             if (valid != KH * KW) {
                 // set weight bits at padded taps = total - in-image rectangle
-                const int total = rect(KH * (KW + 1) + KW);
-                const int inside = rect(r1 * (KW + 1) + c1) - rect(r0 * (KW + 1) + c1) -
-                                   rect(r1 * (KW + 1) + c0) + rect(r0 * (KW + 1) + c0);
-                corr = total - inside;
+                // (c0, c1 are wave-uniform: a select chain, no register indexing)
+                int a0 = 0, a1 = 0, b0 = 0, b1 = 0;
+#pragma unroll
+                for (int c = 0; c <= KW; ++c) {
+                    if (c == c0) { a0 = rt0[c]; a1 = rt1[c]; }
+                    if (c == c1) { b0 = rt0[c]; b1 = rt1[c]; }
+                }
+                corr = rtotal - (b1 - b0 - a1 + a0);
             }
             v = a.in_c * valid - 2 * ((int)acc[p] - corr);
         }
         const float be = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(be_lane), p));
-        store_result_buf(a, orr, (uint32_t)pix, co, v, sc, bi, be);
+        store_result_buf(a, orr, obase + (uint32_t)p * ostep, co, v, sc, bi, be);
     }
 }
 
@@ -266,6 +326,9 @@ hipError_t launch_fast(XArgs a, const Launch &L, int and_mode)
 {
     a.strips_per_row = (a.out_w + P - 1) / P;
     a.strips = (long long)a.n * a.out_h * a.strips_per_row;
+    a.div_tiles = make_fastdiv((uint32_t)a.tiles);
+    a.div_spr = make_fastdiv((uint32_t)a.strips_per_row);
+    a.div_oh = make_fastdiv((uint32_t)a.out_h);
     const long long waves = a.strips * a.tiles;
     const long long blocks = (waves + 3) / 4;
     if (waves * 4 >= 0x7fffffffLL) return hipErrorInvalidValue;
@@ -362,7 +425,7 @@ XArgs make_args(const Geom &g, const uint32_t *bits, const LaneWeights &w, const
     a.tiles = g.tiles;
     a.out_bytes = (int)((long long)g.n * g.out_h * g.out_w * g.out_c * 4);
     a.wlane_bytes = (int)((long long)g.tiles * g.kh * w.kwc4 * 1024);
-    a.wrect_bytes = (int)((long long)g.tiles * (g.kh + 1) * (g.kw + 1) * 256);
+    a.wrect_bytes = (int)((long long)g.tiles * 64 * (g.kh + 1) * rect_row(g.kw) * 4);
     a.apad_bytes = (int)((long long)g.n * g.bits_rows * g.bits_cols * 4);
     a.beta_bytes = (int)((long long)g.n * g.out_h * g.out_w * 4);
     return a;
