@@ -92,8 +92,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void x
     static_assert(CW % CWC == 0, "word chunking");
 
     // Work indices fit 31 bits (the host checks strips * tiles < 2^31).
+    // Workgroups are dealt to the eight XCDs round-robin (block b to XCD
+    // b % 8); renumbering gives XCD x a contiguous run of strips, so its L2
+    // fetches only the input rows of its own part of the batch.  The grid is
+    // a multiple of 8 blocks; blocks past the work exit below.
     const int lane = threadIdx.x & 63;
-    const unsigned gw = blockIdx.x * 4u + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const unsigned per_xcd = gridDim.x >> 3;
+    const unsigned blk = (blockIdx.x & 7u) * per_xcd + (blockIdx.x >> 3);
+    const unsigned gw = blk * 4u + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     // (scalar multiply-high divisions by host-computed reciprocals)
     const unsigned strip = fastdiv(gw, a.div_tiles);
     const unsigned tile = gw - strip * (unsigned)a.tiles;
@@ -330,8 +336,8 @@ hipError_t launch_fast(XArgs a, const Launch &L, int and_mode)
     a.div_spr = make_fastdiv((uint32_t)a.strips_per_row);
     a.div_oh = make_fastdiv((uint32_t)a.out_h);
     const long long waves = a.strips * a.tiles;
-    const long long blocks = (waves + 3) / 4;
-    if (waves * 4 >= 0x7fffffffLL) return hipErrorInvalidValue;
+    const long long blocks = ((waves + 3) / 4 + 7) / 8 * 8;  // a multiple of the 8 XCDs
+    if (blocks * 4 * 4 >= 0x7fffffffLL) return hipErrorInvalidValue;
     if (and_mode)
         return launch_kernel(L, xconv_fast<KH, KW, CW, SW, P, true>, dim3((unsigned)blocks), dim3(256), 0, a);
     return launch_kernel(L, xconv_fast<KH, KW, CW, SW, P, false>, dim3((unsigned)blocks), dim3(256), 0, a);
