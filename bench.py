@@ -11,6 +11,9 @@ HBM.  Prints one JSON line:
              the events do not perturb `value`), against whichever peak binds
              it: the VALU popcount peak (XNOR/AND), the bf16 matrix cores at
              three products per fp32 product (binaryWeights), or HBM;
+  comparison    (XNOR / AND) the same layer through the int8 matrix-core
+             path (BCONV_FLAG_INT8_MFMA), timed the same way, with its own
+             roofline against the dense int8 MFMA peak or HBM;
   cpu_baseline  the CPU oracle timed on a bounded sample of the same layer.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layer I]
@@ -35,6 +38,8 @@ POPCOUNT_PEAK_TBITMAC = VALU_LANE_OPS * 16 / 1e12          # 629.1
 # binaryWeights runs on the bf16 matrix cores (2.5 PFLOP/s dense), three bf16
 # products per exact fp32 product: 2500/3 TFLOP/s of fp32-exact work.
 BF16X3_PEAK_TFLOPS = 2500.0 / 3
+# dense int8 MFMA: 5.0 POP/s = 2.5e15 multiply-accumulates per second
+INT8_PEAK_TMAC = 2500.0
 HBM_PEAK_GBS = 8000.0
 
 
@@ -57,6 +62,22 @@ def algorithmic_bytes(layer, n):
     return src + amap + weights + out
 
 
+def int8_algorithmic_bytes(layer, n):
+    """Bytes the int8 matrix-core kernel must move at least: the int8 input
+    (channels padded to 64, zero halo) once, the A map when beta is on, the
+    int8 weights and the fp32 output."""
+    cpad = (layer.in_c + 63) // 64 * 64
+    if layer.is_fc:
+        rows, cols = layer.in_h, layer.in_w
+    else:
+        rows, cols = layer.in_h + 2 * layer.pad_h, layer.in_w + 2 * layer.pad_w
+    src = n * rows * cols * cpad
+    amap = n * rows * cols * 4 if layer.use_beta else 0
+    weights = layer.out_c * layer.kernel_h * layer.kernel_w * cpad
+    out = n * layer.out_h * layer.out_w * layer.out_c * 4
+    return src + amap + weights + out
+
+
 def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
@@ -66,6 +87,8 @@ def parse():
     p.add_argument("--cpu-images", type=int, default=8,
                    help="images of the layer the oracle runs for cpu_baseline (0: skip)")
     p.add_argument("--cpu-repeats", type=int, default=3)
+    p.add_argument("--no-int8", action="store_true",
+                   help="skip the int8 matrix-core comparison (XNOR / AND layers)")
     p.add_argument("--profile-only", action="store_true",
                    help="run warmup + timed steps and print nothing else (for rocprofv3)")
     p.add_argument("--copy-mib", type=int, default=0,
@@ -119,37 +142,15 @@ def main():
     conv = pca.BinaryConvolution.from_layer(layer, inputs)
     n = layer.n
     x = torch.from_numpy(inputs["x"]).to(dev)
-    out = torch.empty((n, conv.out_h, conv.out_w, conv.out_c), dtype=torch.float32, device=dev)
-    ws_bytes = max(1, conv.workspace_bytes(n))
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     # a dedicated stream at the default priority
     stream = torch.cuda.Stream()
-    sptr = stream.cuda_stream
-
-    for _ in range(args.warmup):
-        pca.bconv_forward(conv.handle, sptr, n, x, out, ws, ws_bytes)
-    torch.cuda.synchronize()
-
-    # timed region 1: K whole forward steps -> value
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for _ in range(args.steps):
-        pca.bconv_forward(conv.handle, sptr, n, x, out, ws, ws_bytes)
-    t1.record(stream)
-    torch.cuda.synchronize()
-
-    # timed region 2: the same K steps, each with hipEvents recorded by the
-    # convolution dispatch itself (hipExtLaunchKernelGGL) -> its duration
-    begins = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    for e in begins + ends:
-        e.record(stream)  # creates the underlying hipEvent
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        pca.bconv_forward_profiled(conv.handle, sptr, n, x, out, ws, ws_bytes,
-                                   begins[i].cuda_event, ends[i].cuda_event)
-    torch.cuda.synchronize()
+    ms_per_step, main_ms, out = time_path(pca, torch, np, conv, n, x, stream, args.warmup, args.steps)
+    conv8 = None
+    if layer.type != "binary_weights" and not args.no_int8:
+        conv8 = pca.BinaryConvolution.from_layer(layer, inputs, int8_mfma=True)
+        ms8, main8, out8 = time_path(pca, torch, np, conv8, n, x, stream, args.warmup, args.steps)
+        diff8 = float((out8 - out).abs().max()) if out.numel() else 0.0
+        del out8
     if args.copy_mib > 0:
         src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -157,9 +158,6 @@ def main():
         torch.cuda.synchronize()
     if args.profile_only:
         return
-    total_ms = t0.elapsed_time(t1)
-    main_ms = float(np.mean([b.elapsed_time(e) for b, e in zip(begins, ends)]))
-    ms_per_step = total_ms / args.steps
     macs = layer.nominal_macs()
     value = macs / (ms_per_step / 1e3) / 1e9
     binary = layer.type != "binary_weights"
@@ -210,12 +208,64 @@ def main():
                      "algorithmic_bytes": nbytes,
                      "avg_kernel_us": round(main_ms * 1e3, 3)},
     }
+    if conv8 is not None:
+        nb8 = int8_algorithmic_bytes(layer, n)
+        if nb8 / (HBM_PEAK_GBS * 1e9) > macs / (INT8_PEAK_TMAC * 1e12):
+            r8 = ("hbm", nb8 / (main8 / 1e3) / 1e9, HBM_PEAK_GBS, "GB/s")
+        else:
+            r8 = ("mfma", macs / (main8 / 1e3) / 1e12, INT8_PEAK_TMAC, "TMAC/s (int8)")
+        line["comparison"] = {"int8_mfma": {
+            "value": round(macs / (ms8 / 1e3) / 1e9, 3), "unit": line["unit"],
+            "ms_per_step": round(ms8, 6), "kernel": conv8.main_kernel(n),
+            "avg_kernel_us": round(main8 * 1e3, 3),
+            "kernel_speed_vs_popcount": round(main_ms / main8, 4),
+            "max_abs_diff_vs_popcount_output": diff8,
+            "roofline": {"bound": r8[0], "achieved": round(r8[1], 3), "peak": r8[2], "unit": r8[3],
+                         "frac": round(r8[1] / r8[2], 4), "algorithmic_bytes": nb8}}}
+        conv8.close()
     if args.cpu_images > 0:
         line["cpu_baseline"] = cpu_baseline(layer, inputs, min(args.cpu_images, n), args.cpu_repeats)
     else:
         line["cpu_baseline"] = None
     conv.close()
     print(json.dumps(line), flush=True)
+
+
+def time_path(pca, torch, np, conv, n, x, stream, warmup, steps):
+    """Warm up, then (1) time `steps` whole forward calls between two stream
+    events, (2) run the same steps again with hipEvents recorded by the main
+    kernel's own dispatch.  Returns (ms per step, mean main-kernel ms, output)."""
+    dev = x.device
+    out = torch.empty((n, conv.out_h, conv.out_w, conv.out_c), dtype=torch.float32, device=dev)
+    ws_bytes = max(1, conv.workspace_bytes(n))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    sptr = stream.cuda_stream
+    for _ in range(warmup):
+        pca.bconv_forward(conv.handle, sptr, n, x, out, ws, ws_bytes)
+    torch.cuda.synchronize()
+
+    # timed region 1: K whole forward steps -> value
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        pca.bconv_forward(conv.handle, sptr, n, x, out, ws, ws_bytes)
+    t1.record(stream)
+    torch.cuda.synchronize()
+
+    # timed region 2: the same K steps, each with hipEvents recorded by the
+    # main kernel's dispatch itself (hipExtLaunchKernelGGL) -> its duration
+    begins = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for e in begins + ends:
+        e.record(stream)  # creates the underlying hipEvent
+    torch.cuda.synchronize()
+    for i in range(steps):
+        pca.bconv_forward_profiled(conv.handle, sptr, n, x, out, ws, ws_bytes,
+                                   begins[i].cuda_event, ends[i].cuda_event)
+    torch.cuda.synchronize()
+    main_ms = float(np.mean([b.elapsed_time(e) for b, e in zip(begins, ends)]))
+    return t0.elapsed_time(t1) / steps, main_ms, out
 
 
 def _kernel_sha() -> str:

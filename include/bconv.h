@@ -78,10 +78,19 @@ typedef enum {
 } bconv_type_t;
 
 /* Flags (MPSCNNBinaryConvolution, Overview, beta paragraph: beta is not an
- * input; a flag turns it on). */
+ * input; a flag turns it on).
+ * BCONV_FLAG_INT8_MFMA selects, for XNOR and AND, a comparison path on the
+ * int8 matrix cores instead of the popcount path: the input is stored as one
+ * int8 per channel (+-1 for XNOR, 0/1 for AND; the products of the type
+ * bullets read on those values), and the window sums are int8 dot products
+ * with int32 accumulation.  Results are identical (exact integers, the same
+ * fp32 epilogue).  The workspace's bits section then holds those int8 values,
+ * channels padded with 0 to a multiple of 64, four per uint32 word
+ * (bits_words = padded channels / 4).  Not valid with BCONV_BINARY_WEIGHTS. */
 enum {
     BCONV_FLAG_NONE = 0u,
-    BCONV_FLAG_USE_BETA_SCALING = 1u
+    BCONV_FLAG_USE_BETA_SCALING = 1u,
+    BCONV_FLAG_INT8_MFMA = 2u
 };
 
 /* The activation applied last (MPSCNNBinaryConvolution, Overview, closing
@@ -110,7 +119,8 @@ typedef struct {
  *   bits:  uint32 [n][bits_rows][bits_cols][bits_words], the binarised input
  *          with a zero halo of bits_pad_h rows and bits_pad_w columns on each
  *          side; channel f of pixel (y,x) is bit (f%32) of word f/32 at row
- *          y + bits_pad_h, column x + bits_pad_w (XNOR and AND only).
+ *          y + bits_pad_h, column x + bits_pad_w (XNOR and AND only; with
+ *          BCONV_FLAG_INT8_MFMA, byte f%4 of word f/4 holds channel f as int8).
  *   a_map: float [n][bits_rows][bits_cols], the A map with the same zero halo
  *          (only with BCONV_FLAG_USE_BETA_SCALING).
  *   beta:  float [n][out_h][out_w] (only with BCONV_FLAG_USE_BETA_SCALING). */

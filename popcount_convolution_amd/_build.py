@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbconv.so")
-SOURCES = ("bconv.hip", "pack.hip", "prepack.hip", "xconv.hip", "bwconv.hip", "bwmma.hip", "gemm.hip")
+SOURCES = ("bconv.hip", "pack.hip", "prepack.hip", "xconv.hip", "bwconv.hip", "bwmma.hip", "gemm.hip", "i8mma.hip")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

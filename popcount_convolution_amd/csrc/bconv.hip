@@ -27,6 +27,8 @@ struct bconv_handle {
     int32_t *d_lane_popc;
     uint32_t *d_flat;         // K-major weights of the fully connected route
     bool gemm;
+    bool i8;                  // int8 matrix-core comparison path (XNOR / AND)
+    void *d_i8frag;           // its int8 weight fragments
     float *d_pm;              // binaryWeights, VALU kernel (+-1.0f table)
     int pm_cols;
     void *d_mma;              // binaryWeights, matrix-core kernel (bf16 fragments)
@@ -67,8 +69,10 @@ bconv_status_t check_desc(const bconv_desc_t *d, int32_t type, uint32_t flags)
     if (!d) return fail(BCONV_ERR_INVALID_ARGUMENT, "desc is NULL");
     if (type != BCONV_BINARY_WEIGHTS && type != BCONV_XNOR && type != BCONV_AND)
         return fail(BCONV_ERR_INVALID_ARGUMENT, "unknown type %d", type);
-    if (flags & ~(uint32_t)BCONV_FLAG_USE_BETA_SCALING)
+    if (flags & ~(uint32_t)(BCONV_FLAG_USE_BETA_SCALING | BCONV_FLAG_INT8_MFMA))
         return fail(BCONV_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", flags);
+    if ((flags & BCONV_FLAG_INT8_MFMA) && type == BCONV_BINARY_WEIGHTS)
+        return fail(BCONV_ERR_INVALID_ARGUMENT, "BCONV_FLAG_INT8_MFMA applies to XNOR and AND only");
     if (d->neuron != BCONV_NEURON_NONE && d->neuron != BCONV_NEURON_RELU)
         return fail(BCONV_ERR_INVALID_ARGUMENT, "unknown neuron %d", d->neuron);
     if (d->groups <= 0) return fail(BCONV_ERR_INVALID_ARGUMENT, "groups must be >= 1");
@@ -133,11 +137,15 @@ bconv_workspace_layout_t layout_for(const bconv_handle *h, int n)
         L.bits_offset = off;
         L.bits_rows = g.bits_rows;
         L.bits_cols = g.bits_cols;
-        L.bits_words = g.words;
+        L.bits_words = h->i8 ? bconv::i8_cpad(g.in_c) / 4 : g.words;
         L.bits_pad_h = g.bits_halo_h;
         L.bits_pad_w = g.bits_halo_w;
-        const size_t words = (size_t)n * g.bits_rows * g.bits_cols * g.words + (size_t)g.bits_slack_words;
-        off = align_up(off + words * 4);
+        if (h->i8) {
+            off = align_up(off + bconv::i8_act_bytes(g));
+        } else {
+            const size_t words = (size_t)n * g.bits_rows * g.bits_cols * g.words + (size_t)g.bits_slack_words;
+            off = align_up(off + words * 4);
+        }
     }
     if (uses_beta(h) && n > 0) {
         // A map with the same zero halo as the bit buffer; beta as written by
@@ -189,7 +197,7 @@ bconv_status_t upload(const T *host, size_t count, T **dev)
 void release(bconv_handle *h)
 {
     if (!h) return;
-    void *ptrs[] = {h->d_lane_words, h->d_lane_popc, h->d_flat, h->d_pm, h->d_mma, h->d_out_scale,
+    void *ptrs[] = {h->d_lane_words, h->d_lane_popc, h->d_flat, h->d_pm, h->d_mma, h->d_i8frag, h->d_out_scale,
                     h->d_out_bias, h->d_in_scale, h->d_in_bias};
     for (void *p : ptrs)
         if (p) (void)hipFree(p);
@@ -238,7 +246,11 @@ bconv_status_t forward_impl(bconv_t h, void *stream, int32_t n, const float *in,
     float *beta = L.beta_offset == SIZE_MAX ? nullptr : reinterpret_cast<float *>(ws + L.beta_offset);
 
     hipError_t e;
-    if (bits || a_map) {
+    if (h->i8) {
+        e = bconv::launch_pack_i8(g, s, in, h->d_in_scale, h->d_in_bias, h->type == BCONV_AND,
+                                  reinterpret_cast<int8_t *>(bits), a_map);
+        if (e != hipSuccess) return hip_fail(e, "int8 pack kernel");
+    } else if (bits || a_map) {
         e = bconv::launch_pack(g, s, in, h->d_in_scale, h->d_in_bias, bits, a_map);
         if (e != hipSuccess) return hip_fail(e, "pack kernel");
     }
@@ -250,7 +262,11 @@ bconv_status_t forward_impl(bconv_t h, void *stream, int32_t n, const float *in,
     ep.beta_out = beta;
     ep.relu = d.neuron == BCONV_NEURON_RELU;
     const bconv::Launch main{s, static_cast<hipEvent_t>(ev_begin), static_cast<hipEvent_t>(ev_end)};
-    if (h->type == BCONV_BINARY_WEIGHTS && !h->force_generic) {
+    if (h->i8) {
+        e = bconv::launch_i8mma(g, main, reinterpret_cast<const int8_t *>(bits), h->d_i8frag, ep,
+                                sink == Sink::Output ? static_cast<float *>(dst) : nullptr,
+                                sink == Sink::Accum ? static_cast<int32_t *>(dst) : nullptr);
+    } else if (h->type == BCONV_BINARY_WEIGHTS && !h->force_generic) {
         e = bconv::launch_bwmma(g, main, in, h->d_in_scale, h->d_in_bias, h->d_mma, ep,
                                 sink == Sink::Output ? static_cast<float *>(dst) : nullptr,
                                 sink == Sink::Accum ? static_cast<float *>(dst) : nullptr);
@@ -361,6 +377,11 @@ bconv_status_t bconv_create(const bconv_desc_t *desc, const uint32_t *weight_bit
     }
     e = bconv::launch_prepack(g, nullptr, d_user, h->d_lane_words, h->d_lane_popc, h->d_pm, h->pm_cols, type);
     if (e == hipSuccess && type == BCONV_BINARY_WEIGHTS) e = bconv::launch_prepack_bwmma(g, nullptr, d_user, h->d_mma);
+    h->i8 = (flags & BCONV_FLAG_INT8_MFMA) != 0;
+    if (e == hipSuccess && h->i8) {
+        e = hipMalloc(&h->d_i8frag, bconv::i8_frag_bytes(g));
+        if (e == hipSuccess) e = bconv::launch_prepack_i8(g, nullptr, d_user, h->d_i8frag, type == BCONV_AND);
+    }
     h->gemm = type != BCONV_BINARY_WEIGHTS && bconv::gemm_route(g);
     if (e == hipSuccess && h->gemm) {
         e = hipMalloc(reinterpret_cast<void **>(&h->d_flat), bconv::gemm_weight_words(g) * 4);
@@ -448,6 +469,7 @@ const char *bconv_main_kernel(bconv_t h, int32_t n)
 {
     if (!h || n < 0) return "";
     const bconv::Geom g = make_geom(h, n);
+    if (h->i8) return bconv::i8mma_kernel_name();
     if (h->type == BCONV_BINARY_WEIGHTS)
         return h->force_generic ? bconv::bwconv_kernel_name(g) : bconv::bwmma_kernel_name(g, h->d_in_scale != nullptr);
     if (h->force_generic) return "xconv_generic";

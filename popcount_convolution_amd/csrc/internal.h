@@ -139,4 +139,15 @@ const char *bwmma_kernel_name(const Geom &g, bool affine);
 hipError_t launch_bwmma(const Geom &g, const Launch &L, const float *x, const float *in_scale, const float *in_bias,
                         const void *frag, const Epilogue &e, float *out, float *acc_out);
 
+// XNOR / AND on the int8 matrix cores (comparison path).
+int i8_cpad(int in_c);  // channels padded to a multiple of 64
+size_t i8_act_bytes(const Geom &g);
+size_t i8_frag_bytes(const Geom &g);
+hipError_t launch_prepack_i8(const Geom &g, hipStream_t s, const uint32_t *user_bits, void *frag, int and_mode);
+hipError_t launch_pack_i8(const Geom &g, hipStream_t s, const float *x, const float *in_scale, const float *in_bias,
+                          int and_mode, int8_t *act, float *a_map);
+const char *i8mma_kernel_name();
+hipError_t launch_i8mma(const Geom &g, const Launch &L, const int8_t *act, const void *frag, const Epilogue &e,
+                        float *out, int32_t *acc_out);
+
 }  // namespace bconv

@@ -48,11 +48,13 @@ def slice_inputs(inputs: dict, images) -> dict:
     return out
 
 
-def run_gpu(layer: workloads.Layer, inputs: dict, device, generic: bool = False) -> dict:
+def run_gpu(layer: workloads.Layer, inputs: dict, device, generic: bool = False,
+            int8_mfma: bool = False) -> dict:
     """Forward and forward_accum through the C ABI; also returns the
-    workspace intermediates (bits, A map, beta) of the forward call."""
+    workspace intermediates (bits or int8 values, A map, beta) of the forward
+    call.  ``int8_mfma`` selects the int8 matrix-core comparison path."""
     with force_generic(generic):
-        conv = pca.BinaryConvolution.from_layer(layer, inputs)
+        conv = pca.BinaryConvolution.from_layer(layer, inputs, int8_mfma=int8_mfma)
     try:
         n = inputs["x"].shape[0]
         x = torch.from_numpy(inputs["x"]).to(device)
@@ -73,8 +75,11 @@ def run_gpu(layer: workloads.Layer, inputs: dict, device, generic: bool = False)
         wsh = ws.cpu().numpy()
         if L["bits_offset"] is not None:
             cnt = n * L["bits_rows"] * L["bits_cols"] * L["bits_words"]
-            words = wsh[L["bits_offset"]:L["bits_offset"] + 4 * cnt].view("<u4")
-            res["bits"] = words.reshape(n, L["bits_rows"], L["bits_cols"], L["bits_words"])
+            raw = wsh[L["bits_offset"]:L["bits_offset"] + 4 * cnt]
+            if int8_mfma:
+                res["int8"] = raw.view(np.int8).reshape(n, L["bits_rows"], L["bits_cols"], 4 * L["bits_words"])
+            else:
+                res["bits"] = raw.view("<u4").reshape(n, L["bits_rows"], L["bits_cols"], L["bits_words"])
             res["bits_pad"] = (L["bits_pad_h"], L["bits_pad_w"])
         if L["a_map_offset"] is not None:
             rows, cols = L["bits_rows"], L["bits_cols"]
@@ -159,6 +164,16 @@ def compare(layer: workloads.Layer, inputs: dict, got: dict, ref: dict = None, i
         halo = g["bits"].copy()
         halo[:, ph:ph + h, pw:pw + w, :] = 0
         assert not halo.any(), f"{layer.name}: halo of the packed input is not zero"
+    if "int8" in g and ref.get("signs") is not None:
+        ph, pw = got["bits_pad"]
+        h, w, c = layer.in_h, layer.in_w, layer.in_c
+        neg = 0 if layer.type == "and" else -1
+        want = np.where(ref["signs"] > 0, 1, neg).astype(np.int8)
+        inner = g["int8"][:, ph:ph + h, pw:pw + w, :c]
+        assert np.array_equal(inner, want), f"{layer.name}: int8 input values differ"
+        rest = g["int8"].copy()
+        rest[:, ph:ph + h, pw:pw + w, :c] = 0
+        assert not rest.any(), f"{layer.name}: int8 halo or channel padding is not zero"
     if layer.use_beta:
         assert got["a_halo_zero"], f"{layer.name}: halo of the A map is not zero"
         np.testing.assert_allclose(g["a_map"], ref["a_map"], rtol=RTOL, atol=0,

@@ -54,7 +54,10 @@ def _desc(**kw):
     (dict(groups=2), pca.BCONV_XNOR, 0, pca.BCONV_ERR_UNSUPPORTED),
     (dict(groups=0), pca.BCONV_XNOR, 0, pca.BCONV_ERR_INVALID_ARGUMENT),
     ({}, 3, 0, pca.BCONV_ERR_INVALID_ARGUMENT),
-    ({}, pca.BCONV_XNOR, 2, pca.BCONV_ERR_INVALID_ARGUMENT),
+    ({}, pca.BCONV_XNOR, pca.BCONV_FLAG_INT8_MFMA, pca.BCONV_OK),
+    ({}, pca.BCONV_AND, pca.BCONV_FLAG_INT8_MFMA | 1, pca.BCONV_OK),
+    ({}, pca.BCONV_BINARY_WEIGHTS, pca.BCONV_FLAG_INT8_MFMA, pca.BCONV_ERR_INVALID_ARGUMENT),
+    ({}, pca.BCONV_XNOR, 4, pca.BCONV_ERR_INVALID_ARGUMENT),
     (dict(neuron=2), pca.BCONV_XNOR, 0, pca.BCONV_ERR_INVALID_ARGUMENT),
     (dict(in_h=0), pca.BCONV_XNOR, 0, pca.BCONV_ERR_INVALID_ARGUMENT),
     (dict(in_c=-1), pca.BCONV_XNOR, 0, pca.BCONV_ERR_INVALID_ARGUMENT),

@@ -182,6 +182,57 @@ def test_binary_weights_special_values(dev):
         assert np.any(g[1] != 0) and np.any(g[2] != 0), "tiny values must not flush to zero"
 
 
+# ------------------------------------------------ int8 matrix-core comparison path
+
+def _int8_layers():
+    base = workloads.Layer("i8", "xnor", 2, 9, 10, 64, 70, 3, 3, 1, 1, 1, 1)
+    geoms = [
+        dict(name="i8_bench", **{k: getattr(workloads.BENCH_LAYER, k) for k in (
+            "type", "in_h", "in_w", "in_c", "out_c", "use_beta", "neuron", "iscale_dist", "ibias_dist")}),
+        dict(name="i8_and", type="and", n=2, in_h=28, in_w=28, in_c=256, out_c=256, x_dist=("normal", 0.2, 1.0)),
+        dict(name="i8_small", n=1, in_h=16, in_w=16, in_c=64, out_c=64),
+        dict(name="i8_ragged", n=3, in_h=11, in_w=19, in_c=100, out_c=130, use_beta=True, neuron="relu"),
+        dict(name="i8_cin33", type="and", n=1, in_h=5, in_w=7, in_c=33, out_c=65),
+        dict(name="i8_s2", n=2, in_h=14, in_w=14, in_c=256, out_c=64, stride_h=2, stride_w=2),
+        dict(name="i8_1x1", n=2, in_h=10, in_w=12, in_c=64, out_c=64, kernel_h=1, kernel_w=1, pad_h=0, pad_w=0),
+        dict(name="i8_5x5", n=1, in_h=12, in_w=11, in_c=64, out_c=33, kernel_h=5, kernel_w=5, pad_h=2, pad_w=2),
+        dict(name="i8_fc", n=3, in_h=4, in_w=5, in_c=37, out_c=66, kernel_h=4, kernel_w=5, pad_h=0, pad_w=0),
+        dict(name="i8_1px", n=1, in_h=1, in_w=1, in_c=64, out_c=8),
+    ]
+    return [base.with_(**g) for g in geoms]
+
+
+INT8_LAYERS = _int8_layers()
+INT8_MEASURED = [i for i, l in enumerate(workloads.LAYERS) if l.type != "binary_weights"]
+
+
+@pytest.mark.parametrize("index", INT8_MEASURED, ids=[workloads.LAYERS[i].name for i in INT8_MEASURED])
+def test_int8_mfma_measured_layer_sampled(dev, index):
+    """The int8 path on each XNOR / AND measured layer at full size, sampled
+    as in the popcount path's measured-layer test."""
+    layer = workloads.LAYERS[index]
+    inputs = workloads.make_inputs(layer, workloads.layer_seed(index))
+    _log(f"int8 layer {layer.name} seed {workloads.layer_seed(index)}")
+    got = parity.run_gpu(layer, inputs, dev, int8_mfma=True)
+    assert got["main_kernel"] == "i8mma_kernel"
+    n = layer.n
+    images = sorted({0, 1, n - 1}) if layer.is_fc else sorted({0, n - 1})
+    parity.compare(layer, inputs, got, images=np.array(images))
+
+
+@pytest.mark.parametrize("layer", INT8_LAYERS, ids=[l.name for l in INT8_LAYERS])
+def test_int8_mfma_path(dev, layer):
+    """BCONV_FLAG_INT8_MFMA: the same exact window sums and epilogue as the
+    popcount path, and the int8 values of the workspace are the oracle's
+    binarised input with a zero halo and zero channel padding."""
+    inputs = workloads.make_inputs(layer, 7000 + INT8_LAYERS.index(layer))
+    _log(f"int8 {layer}")
+    ref = oracle.bconv_layer(layer, inputs)
+    got = parity.run_gpu(layer, inputs, dev, int8_mfma=True)
+    assert got["main_kernel"] == "i8mma_kernel"
+    parity.compare(layer, inputs, got, ref=ref)
+
+
 # ------------------------------------------------------------ robustness
 
 def test_repeat_is_bit_identical(dev):
