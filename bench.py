@@ -174,15 +174,8 @@ def main():
         bound, achieved, peak, runit = "hbm", nbytes / (main_ms / 1e3) / 1e9, HBM_PEAK_GBS, "GB/s"
     else:
         bound, achieved, peak, runit = cmp
-    traffic = None
-    tfile = os.path.join(ROOT, "profiles", "traffic.json")
     kernel = conv.main_kernel(n)
-    if os.path.exists(tfile):
-        with open(tfile) as f:
-            t = json.load(f)
-        entry = t.get(layer.name)
-        if entry and entry.get("kernel") == kernel and entry.get("source_sha") == _kernel_sha():
-            traffic = entry.get("bytes_per_launch")
+    traffic = recorded_traffic(layer.name, kernel)
     line = {
         "metric": "binary conv GOPS (bit-MACs/s) and % of VALU popcount peak, 1 MI355X",
         "value": round(value, 3),
@@ -214,14 +207,16 @@ def main():
             r8 = ("hbm", nb8 / (main8 / 1e3) / 1e9, HBM_PEAK_GBS, "GB/s")
         else:
             r8 = ("mfma", macs / (main8 / 1e3) / 1e12, INT8_PEAK_TMAC, "TMAC/s (int8)")
+        k8 = conv8.main_kernel(n)
         line["comparison"] = {"int8_mfma": {
             "value": round(macs / (ms8 / 1e3) / 1e9, 3), "unit": line["unit"],
-            "ms_per_step": round(ms8, 6), "kernel": conv8.main_kernel(n),
+            "ms_per_step": round(ms8, 6), "kernel": k8,
             "avg_kernel_us": round(main8 * 1e3, 3),
             "kernel_speed_vs_popcount": round(main_ms / main8, 4),
             "max_abs_diff_vs_popcount_output": diff8,
             "roofline": {"bound": r8[0], "achieved": round(r8[1], 3), "peak": r8[2], "unit": r8[3],
-                         "frac": round(r8[1] / r8[2], 4), "algorithmic_bytes": nb8}}}
+                         "frac": round(r8[1] / r8[2], 4), "algorithmic_bytes": nb8,
+                         "traffic": recorded_traffic(layer.name + "#int8_mfma", k8)}}}
         conv8.close()
     if args.cpu_images > 0:
         line["cpu_baseline"] = cpu_baseline(layer, inputs, min(args.cpu_images, n), args.cpu_repeats)
@@ -268,14 +263,35 @@ def time_path(pca, torch, np, conv, n, x, stream, warmup, steps):
     return t0.elapsed_time(t1) / steps, main_ms, out
 
 
-def _kernel_sha() -> str:
+# the source file that defines (and launches) each main kernel
+KERNEL_FILES = {"xconv": "xconv.hip", "bgemm": "gemm.hip", "bwmma": "bwmma.hip", "bwconv": "bwconv.hip",
+                "i8mma": "i8mma.hip"}
+
+
+def _kernel_sha(kernel: str) -> str:
+    """Hash of the sources a main kernel is built from (its own file and the
+    shared internal header): recorded traffic stays valid while it matches."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "popcount_convolution_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    prefix = kernel.split("<")[0].split("_")[0]
+    for name in (KERNEL_FILES[prefix], "internal.h"):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
+
+
+def recorded_traffic(key: str, kernel: str):
+    """HBM bytes per launch recorded under profiles/ for `key`, or None when
+    absent or taken from other kernel sources."""
+    tfile = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(tfile):
+        return None
+    with open(tfile) as f:
+        entry = json.load(f).get(key)
+    if entry and entry.get("kernel") == kernel and entry.get("source_sha") == _kernel_sha(kernel):
+        return entry.get("bytes_per_launch")
+    return None
 
 
 if __name__ == "__main__":
