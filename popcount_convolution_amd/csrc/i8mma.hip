@@ -165,6 +165,7 @@ struct I8Args {
     int n, out_c, out_h, out_w, kh, kw, sh, sw, rows, cols, cpad;
     int chunks, ksteps, ntiles, mtiles, m_total;
     int act_bytes, out_bytes, vec_out;
+    int weights_major;  // consecutive tiles share a weight tile (weights outweigh activations)
 };
 
 __global__ __launch_bounds__(kThreads) void i8mma_kernel(I8Args a)
@@ -174,12 +175,21 @@ __global__ __launch_bounds__(kThreads) void i8mma_kernel(I8Args a)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int group = wave & 3, khalf = wave >> 2;
     // XCD-aware numbering: block b runs on XCD b % 8; XCD x takes the
-    // contiguous tile range [x*per, (x+1)*per).
+    // contiguous tile range [x*per, (x+1)*per).  Within it the larger operand
+    // changes slowest, so the workgroups that share its tile run together
+    // and read it through one L2.
     const int blocks = a.mtiles * a.ntiles;
     const int per = (blocks + kXcds - 1) / kXcds;
     const int idx = (int)(blockIdx.x % kXcds) * per + (int)(blockIdx.x / kXcds);
     if (idx >= blocks) return;  // uniform over the workgroup
-    const int mtile = idx / a.ntiles, ntile = idx - (idx / a.ntiles) * a.ntiles;
+    int mtile, ntile;
+    if (a.weights_major) {
+        ntile = idx / a.mtiles;
+        mtile = idx - ntile * a.mtiles;
+    } else {
+        mtile = idx / a.ntiles;
+        ntile = idx - mtile * a.ntiles;
+    }
 
     // this lane's output pixel (pixels past the batch reuse the last one and
     // are not stored)
@@ -411,6 +421,7 @@ hipError_t launch_i8mma(const Geom &g, const Launch &L, const int8_t *act, const
     a.out_bytes = (int)out_bytes;
     const void *dst = acc_out ? (const void *)acc_out : (const void *)out;
     a.vec_out = g.out_c % 4 == 0 && (uintptr_t)dst % 16 == 0;
+    a.weights_major = (long long)a.ntiles * a.ksteps * kStepU4 * 16 > act_bytes;
     const int blocks = a.mtiles * a.ntiles;
     const int grid = (blocks + kXcds - 1) / kXcds * kXcds;
     const uint32_t stage_bytes = (uint32_t)(a.ksteps < kStage ? a.ksteps : kStage) * kStepU4 * 16;
