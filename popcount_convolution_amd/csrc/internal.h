@@ -34,6 +34,14 @@ constexpr int kBufferFlags = 0x00020000;
 // Buffer cache policy: agent-scope write-through (sc1).
 constexpr int kStoreSc1 = 16;
 
+// Agent-scope relaxed store: written through to memory while the kernel runs,
+// so it does not sit dirty in one XCD's L2 until the end-of-kernel write-back.
+template <typename T>
+__device__ __forceinline__ void store_through(T *p, T v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, int bytes)
 {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, bytes, kBufferFlags);
@@ -80,18 +88,20 @@ __host__ __device__ inline int rect_row(int kw) { return (kw + 1 + 3) / 4 * 4; }
 struct FastDiv {
     uint32_t m;
     int s;
+    uint32_t id;  // all ones for d <= 1 (m = 0, quotient = n), else 0
 };
 inline FastDiv make_fastdiv(uint32_t d)
 {
-    if (d <= 1) return FastDiv{0u, 0};
+    if (d <= 1) return FastDiv{0u, 0, 0xffffffffu};
     int l = 0;
     while ((1ull << l) < d) ++l;
     const unsigned long long m = (1ull << (31 + l)) / d + 1;
-    return FastDiv{(uint32_t)m, l - 1};
+    return FastDiv{(uint32_t)m, l - 1, 0u};
 }
+// Branch-free: for d <= 1 the product term is 0 and the mask passes n.
 __device__ __forceinline__ uint32_t fastdiv(uint32_t n, FastDiv f)
 {
-    return f.m ? (__umulhi(n, f.m) >> f.s) : n;
+    return (__umulhi(n, f.m) >> f.s) | (n & f.id);
 }
 
 // Epilogue operands.  With a_pad set, the convolution kernels form beta as

@@ -62,11 +62,11 @@ __device__ void clear_halo(const PackArgs &a, long long t)
         const unsigned img = u / per;
         int row, col;
         halo_pixel(a, u - img * per, row, col);
-        a.a_map[((long long)img * a.rows + row) * a.cols + col] = 0.0f;
+        store_through(&a.a_map[((long long)img * a.rows + row) * a.cols + col], 0.0f);
         return;
     }
     if (t >= a.halo_words) {
-        a.bits[(long long)a.n * a.image_words + (t - a.halo_words)] = 0u;
+        store_through(&a.bits[(long long)a.n * a.image_words + (t - a.halo_words)], 0u);
         return;
     }
     const unsigned u = (unsigned)t;
@@ -76,7 +76,7 @@ __device__ void clear_halo(const PackArgs &a, long long t)
     const unsigned word = r % (unsigned)a.words;
     int row, col;
     halo_pixel(a, r / (unsigned)a.words, row, col);
-    a.bits[(long long)img * a.image_words + ((long long)row * a.cols + col) * a.words + word] = 0u;
+    store_through(&a.bits[(long long)img * a.image_words + ((long long)row * a.cols + col) * a.words + word], 0u);
 }
 
 // Pixel indices fit 31 bits (the host checks), so the decomposition uses
@@ -204,7 +204,7 @@ __global__ __launch_bounds__(256) void pack_vec4(PackArgs a)
             if (a.bits) {
                 const uint32_t word = group_or<LPW>(nib << ((sl * 4) & 31));
                 if (cact && px < a.in_w && (sl % LPW) == 0)
-                    a.bits[((long long)pad_base + u * G + slot) * a.words + c / 32] = word;
+                    store_through(&a.bits[((long long)pad_base + u * G + slot) * a.words + c / 32], word);
             }
         }
     }
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(256) void pack_vec4(PackArgs a)
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const float s = group_sum<SEG>(asum[u]);
-            if (sl == 0 && x0 + u * G + slot < a.in_w) a.a_map[(long long)pad_base + u * G + slot] = s * inv_c;
+            if (sl == 0 && x0 + u * G + slot < a.in_w) store_through(&a.a_map[(long long)pad_base + u * G + slot], s * inv_c);
         }
     }
 }
@@ -273,13 +273,13 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a)
             uint32_t part = nib << ((sl * VEC) & 31);
 #pragma unroll
             for (int off = 1; off < LPW; off <<= 1) part |= __shfl_xor(part, off, 64);
-            if (act && (sl % LPW) == 0) a.bits[dst + c / 32] = part;
+            if (act && (sl % LPW) == 0) store_through(&a.bits[dst + c / 32], part);
         }
     }
     if (a.a_map) {
 #pragma unroll
         for (int off = 1; off < SEG; off <<= 1) asum += __shfl_xor(asum, off, 64);
-        if (live && sl == 0) a.a_map[padded_pixel(a, pix)] = asum / (float)a.in_c;
+        if (live && sl == 0) store_through(&a.a_map[padded_pixel(a, pix)], asum / (float)a.in_c);
     }
 }
 
