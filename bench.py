@@ -13,7 +13,9 @@ HBM.  Prints one JSON line:
              three products per fp32 product (binaryWeights), or HBM;
   comparison    (XNOR / AND) the same layer through the int8 matrix-core
              path (BCONV_FLAG_INT8_MFMA), timed the same way, with its own
-             roofline against the dense int8 MFMA peak or HBM;
+             roofline against the dense int8 MFMA peak or HBM; and the layer
+             with its output written as packed sign bits for a next binary
+             layer (bconv_forward_bits), timed the same way;
   cpu_baseline  the CPU oracle timed on a bounded sample of the same layer.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layer I]
@@ -43,10 +45,11 @@ INT8_PEAK_TMAC = 2500.0
 HBM_PEAK_GBS = 8000.0
 
 
-def algorithmic_bytes(layer, n):
+def algorithmic_bytes(layer, n, bits_out=False):
     """Bytes the convolution / matrix kernel must move at least: its input
     operand once (packed bits for XNOR/AND, fp32 for binaryWeights), the A
-    map when beta is on, the weight bits and the fp32 output."""
+    map when beta is on, the weight bits and the output (fp32, or packed sign
+    bits with `bits_out`)."""
     words = (layer.in_c + 31) // 32
     if layer.is_fc:
         rows, cols = layer.in_h, layer.in_w
@@ -58,7 +61,7 @@ def algorithmic_bytes(layer, n):
         src = n * rows * cols * words * 4
     amap = n * rows * cols * 4 if layer.use_beta else 0
     weights = layer.out_c * layer.kernel_h * layer.kernel_w * words * 4
-    out = n * layer.out_h * layer.out_w * layer.out_c * 4
+    out = n * layer.out_h * layer.out_w * (((layer.out_c + 31) // 32) if bits_out else layer.out_c) * 4
     return src + amap + weights + out
 
 
@@ -89,6 +92,8 @@ def parse():
     p.add_argument("--cpu-repeats", type=int, default=3)
     p.add_argument("--no-int8", action="store_true",
                    help="skip the int8 matrix-core comparison (XNOR / AND layers)")
+    p.add_argument("--no-bits", action="store_true",
+                   help="skip the packed sign-bit output comparison")
     p.add_argument("--profile-only", action="store_true",
                    help="run warmup + timed steps and print nothing else (for rocprofv3)")
     p.add_argument("--copy-mib", type=int, default=0,
@@ -151,6 +156,9 @@ def main():
         ms8, main8, out8 = time_path(pca, torch, np, conv8, n, x, stream, args.warmup, args.steps)
         diff8 = float((out8 - out).abs().max()) if out.numel() else 0.0
         del out8
+    if not args.no_bits:
+        msb, mainb, outb = time_path(pca, torch, np, conv, n, x, stream, args.warmup, args.steps, bits=True)
+        del outb
     if args.copy_mib > 0:
         src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -218,6 +226,20 @@ def main():
                          "frac": round(r8[1] / r8[2], 4), "algorithmic_bytes": nb8,
                          "traffic": recorded_traffic(layer.name + "#int8_mfma", k8)}}}
         conv8.close()
+    if not args.no_bits:
+        nbb = algorithmic_bytes(layer, n, bits_out=True)
+        if nbb / (HBM_PEAK_GBS * 1e9) > t_cmp:
+            rb = ("hbm", nbb / (mainb / 1e3) / 1e9, HBM_PEAK_GBS, "GB/s")
+        elif binary:
+            rb = ("alu", macs / (mainb / 1e3) / 1e12, POPCOUNT_PEAK_TBITMAC, "Tbit-MAC/s")
+        else:
+            rb = ("mfma", 2 * macs / (mainb / 1e3) / 1e12, BF16X3_PEAK_TFLOPS, "TFLOP/s (fp32-exact, bf16x3)")
+        line.setdefault("comparison", {})["packed_bits_output"] = {
+            "value": round(macs / (msb / 1e3) / 1e9, 3), "unit": line["unit"],
+            "ms_per_step": round(msb, 6), "kernel": kernel, "avg_kernel_us": round(mainb * 1e3, 3),
+            "output_bytes": (n * layer.out_h * layer.out_w * ((layer.out_c + 31) // 32) * 4),
+            "roofline": {"bound": rb[0], "achieved": round(rb[1], 3), "peak": rb[2], "unit": rb[3],
+                         "frac": round(rb[1] / rb[2], 4), "algorithmic_bytes": nbb}}
     if args.cpu_images > 0:
         line["cpu_baseline"] = cpu_baseline(layer, inputs, min(args.cpu_images, n), args.cpu_repeats)
     else:
@@ -226,17 +248,23 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def time_path(pca, torch, np, conv, n, x, stream, warmup, steps):
+def time_path(pca, torch, np, conv, n, x, stream, warmup, steps, bits=False):
     """Warm up, then (1) time `steps` whole forward calls between two stream
     events, (2) run the same steps again with hipEvents recorded by the main
-    kernel's own dispatch.  Returns (ms per step, mean main-kernel ms, output)."""
+    kernel's own dispatch.  Returns (ms per step, mean main-kernel ms, output).
+    With `bits` the output is the packed sign-bit form (bconv_forward_bits)."""
     dev = x.device
-    out = torch.empty((n, conv.out_h, conv.out_w, conv.out_c), dtype=torch.float32, device=dev)
+    if bits:
+        out = torch.empty((n, conv.out_h, conv.out_w, (conv.out_c + 31) // 32), dtype=torch.int32, device=dev)
+        fwd, fwd_prof = pca.bconv_forward_bits, pca.bconv_forward_bits_profiled
+    else:
+        out = torch.empty((n, conv.out_h, conv.out_w, conv.out_c), dtype=torch.float32, device=dev)
+        fwd, fwd_prof = pca.bconv_forward, pca.bconv_forward_profiled
     ws_bytes = max(1, conv.workspace_bytes(n))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     sptr = stream.cuda_stream
     for _ in range(warmup):
-        pca.bconv_forward(conv.handle, sptr, n, x, out, ws, ws_bytes)
+        fwd(conv.handle, sptr, n, x, out, ws, ws_bytes)
     torch.cuda.synchronize()
 
     # timed region 1: K whole forward steps -> value
@@ -244,7 +272,7 @@ def time_path(pca, torch, np, conv, n, x, stream, warmup, steps):
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record(stream)
     for _ in range(steps):
-        pca.bconv_forward(conv.handle, sptr, n, x, out, ws, ws_bytes)
+        fwd(conv.handle, sptr, n, x, out, ws, ws_bytes)
     t1.record(stream)
     torch.cuda.synchronize()
 
@@ -256,8 +284,7 @@ def time_path(pca, torch, np, conv, n, x, stream, warmup, steps):
         e.record(stream)  # creates the underlying hipEvent
     torch.cuda.synchronize()
     for i in range(steps):
-        pca.bconv_forward_profiled(conv.handle, sptr, n, x, out, ws, ws_bytes,
-                                   begins[i].cuda_event, ends[i].cuda_event)
+        fwd_prof(conv.handle, sptr, n, x, out, ws, ws_bytes, begins[i].cuda_event, ends[i].cuda_event)
     torch.cuda.synchronize()
     main_ms = float(np.mean([b.elapsed_time(e) for b, e in zip(begins, ends)]))
     return t0.elapsed_time(t1) / steps, main_ms, out

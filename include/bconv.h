@@ -200,6 +200,26 @@ bconv_status_t bconv_forward_profiled(bconv_t h, void *stream, int32_t n, const 
                                       float *out, void *workspace, size_t workspace_bytes,
                                       void *main_begin, void *main_end);
 
+/* As bconv_forward, but the convolution's epilogue writes packed sign bits of
+ * its fp32 output instead of the values, in the input encoding of a next
+ * binary layer (Apple "MPSCNNBinaryConvolution", Overview: the XNOR and AND
+ * bullets read a value as +1 / 1 unless it is below 0).  `out_bits` is device
+ * memory of n*out_h*out_w*ceil(out_c/32) uint32 words, NHWC: channel c of
+ * pixel (b, y, x) is bit c % 32 (least significant first) of word
+ * ((b*out_h + y)*out_w + x)*ceil(out_c/32) + c/32; the bit is 1 unless the
+ * value bconv_forward would write is < 0 (so +-0 and NaN give 1, and every bit
+ * is 1 under ReLU); bits past out_c are 0.  The fp32 output is not written.
+ * Same errors as bconv_forward; `out_bits` must not overlap `in` or the
+ * workspace. */
+bconv_status_t bconv_forward_bits(bconv_t h, void *stream, int32_t n, const float *in,
+                                  uint32_t *out_bits, void *workspace, size_t workspace_bytes);
+
+/* As bconv_forward_bits, with the hipEvents of bconv_forward_profiled. */
+bconv_status_t bconv_forward_bits_profiled(bconv_t h, void *stream, int32_t n, const float *in,
+                                           uint32_t *out_bits, void *workspace,
+                                           size_t workspace_bytes, void *main_begin,
+                                           void *main_end);
+
 /* Name of the kernel bconv_forward_profiled brackets for batch n (a static
  * string; "" for an invalid handle). */
 const char *bconv_main_kernel(bconv_t h, int32_t n);

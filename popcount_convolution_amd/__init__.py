@@ -19,7 +19,8 @@ from ._binding import (  # noqa: F401  (re-exported C ABI names)
     BCONV_ERR_UNSUPPORTED, BCONV_ERR_WORKSPACE, BCONV_FLAG_INT8_MFMA, BCONV_FLAG_NONE, BCONV_FLAG_USE_BETA_SCALING,
     BCONV_NEURON_NONE, BCONV_NEURON_RELU, BCONV_OK, BCONV_XNOR, NEURON_CODES, TYPE_CODES,
     BconvError, BconvLibraryMissing, bconv_create, bconv_create_fc, bconv_desc_t, bconv_destroy,
-    bconv_forward, bconv_forward_accum, bconv_forward_profiled, bconv_get_info, bconv_last_error,
+    bconv_forward, bconv_forward_accum, bconv_forward_bits, bconv_forward_bits_profiled, bconv_forward_profiled,
+    bconv_get_info, bconv_last_error,
     bconv_main_kernel, bconv_status_string, bconv_validate_desc, bconv_workspace_layout,
     bconv_workspace_size, load_library, make_desc)
 
@@ -95,6 +96,23 @@ class BinaryConvolution:
         bconv_forward_accum(self.handle, self._stream(stream), n, x, acc, workspace,
                             workspace.numel() * workspace.element_size())
         return acc
+
+    def out_words(self) -> int:
+        return (self.out_c + 31) // 32
+
+    def forward_bits(self, x, out_bits=None, workspace=None, stream=None):
+        """Packed sign bits of the output (see bconv_forward_bits), as int32
+        words [n, out_h, out_w, ceil(out_c/32)] holding the uint32 bit patterns."""
+        import torch
+        n = x.shape[0]
+        if out_bits is None:
+            out_bits = torch.empty((n, self.out_h, self.out_w, self.out_words()), dtype=torch.int32,
+                                   device=x.device)
+        if workspace is None:
+            workspace = self.workspace(n, x.device)
+        bconv_forward_bits(self.handle, self._stream(stream), n, x, out_bits, workspace,
+                           workspace.numel() * workspace.element_size())
+        return out_bits
 
     def main_kernel(self, n: int) -> str:
         return bconv_main_kernel(self.handle, n)

@@ -94,6 +94,8 @@ def load_library(path: Optional[str] = None):
         "bconv_forward": (st, [vp, vp, i32, vp, vp, vp, sz]),
         "bconv_forward_accum": (st, [vp, vp, i32, vp, vp, vp, sz]),
         "bconv_forward_profiled": (st, [vp, vp, i32, vp, vp, vp, sz, vp, vp]),
+        "bconv_forward_bits": (st, [vp, vp, i32, vp, vp, vp, sz]),
+        "bconv_forward_bits_profiled": (st, [vp, vp, i32, vp, vp, vp, sz, vp, vp]),
         "bconv_main_kernel": (ctypes.c_char_p, [vp, i32]),
         "bconv_destroy": (st, [vp]),
         "bconv_status_string": (ctypes.c_char_p, [st]),
@@ -210,6 +212,18 @@ def bconv_forward_profiled(h: int, stream, n: int, inp, out, workspace, workspac
     _check(load_library().bconv_forward_profiled(h, _ptr(stream), n, _ptr(inp), _ptr(out),
                                                  _ptr(workspace), workspace_bytes,
                                                  _ptr(main_begin), _ptr(main_end)))
+
+
+def bconv_forward_bits(h: int, stream, n: int, inp, out_bits, workspace, workspace_bytes: int) -> None:
+    _check(load_library().bconv_forward_bits(h, _ptr(stream), n, _ptr(inp), _ptr(out_bits), _ptr(workspace),
+                                             workspace_bytes))
+
+
+def bconv_forward_bits_profiled(h: int, stream, n: int, inp, out_bits, workspace, workspace_bytes: int,
+                                main_begin=None, main_end=None) -> None:
+    _check(load_library().bconv_forward_bits_profiled(h, _ptr(stream), n, _ptr(inp), _ptr(out_bits),
+                                                      _ptr(workspace), workspace_bytes,
+                                                      _ptr(main_begin), _ptr(main_end)))
 
 
 def bconv_main_kernel(h: int, n: int) -> str:

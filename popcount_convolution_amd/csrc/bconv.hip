@@ -210,7 +210,9 @@ bool ranges_overlap(const void *a, size_t an, const void *b, size_t bn)
     return a0 < b0 + bn && b0 < a0 + an;
 }
 
-enum class Sink { Output, Accum };
+// Output forms: fp32 values, raw window sums, or packed sign bits of the
+// fp32 values ([n][out_h][out_w][ceil(out_c/32)] words).
+enum class Sink { Output, Accum, Bits };
 
 bconv_status_t forward_impl(bconv_t h, void *stream, int32_t n, const float *in, void *dst, Sink sink,
                             void *workspace, size_t workspace_bytes, void *ev_begin, void *ev_end)
@@ -221,7 +223,9 @@ bconv_status_t forward_impl(bconv_t h, void *stream, int32_t n, const float *in,
     if (!in || !dst) return fail(BCONV_ERR_INVALID_ARGUMENT, "in/out must not be NULL");
     const bconv_desc_t &d = h->desc;
     const size_t in_bytes = (size_t)n * d.in_h * d.in_w * d.in_c * 4;
-    const size_t out_bytes = (size_t)n * h->out_h * h->out_w * d.out_c * 4;
+    const int out_words = (d.out_c + 31) / 32;
+    const size_t out_bytes =
+        (size_t)n * h->out_h * h->out_w * (sink == Sink::Bits ? (size_t)out_words : (size_t)d.out_c) * 4;
     if (ranges_overlap(in, in_bytes, dst, out_bytes))
         return fail(BCONV_ERR_INVALID_ARGUMENT, "input and output overlap");
     if ((long long)n * d.in_h * d.in_w >= (1LL << 31) || (long long)n * h->out_h * h->out_w * h->tiles >= (1LL << 29) ||
@@ -261,6 +265,10 @@ bconv_status_t forward_impl(bconv_t h, void *stream, int32_t n, const float *in,
     ep.a_pad = a_map;
     ep.beta_out = beta;
     ep.relu = d.neuron == BCONV_NEURON_RELU;
+    if (sink == Sink::Bits) {
+        ep.bits_out = static_cast<uint32_t *>(dst);
+        ep.out_words = out_words;
+    }
     const bconv::Launch main{s, static_cast<hipEvent_t>(ev_begin), static_cast<hipEvent_t>(ev_end)};
     if (h->i8) {
         e = bconv::launch_i8mma(g, main, reinterpret_cast<const int8_t *>(bits), h->d_i8frag, ep,
@@ -462,6 +470,20 @@ bconv_status_t bconv_forward_profiled(bconv_t h, void *stream, int32_t n, const 
                                       void *main_end)
 {
     return forward_impl(h, stream, n, in, out, Sink::Output, workspace, workspace_bytes, main_begin,
+                        main_end);
+}
+
+bconv_status_t bconv_forward_bits(bconv_t h, void *stream, int32_t n, const float *in, uint32_t *out_bits,
+                                  void *workspace, size_t workspace_bytes)
+{
+    return forward_impl(h, stream, n, in, out_bits, Sink::Bits, workspace, workspace_bytes, nullptr, nullptr);
+}
+
+bconv_status_t bconv_forward_bits_profiled(bconv_t h, void *stream, int32_t n, const float *in,
+                                           uint32_t *out_bits, void *workspace, size_t workspace_bytes,
+                                           void *main_begin, void *main_end)
+{
+    return forward_impl(h, stream, n, in, out_bits, Sink::Bits, workspace, workspace_bytes, main_begin,
                         main_end);
 }
 

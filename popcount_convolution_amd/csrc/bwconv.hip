@@ -28,6 +28,8 @@ struct BwArgs {
     int relu;
     float *out;
     float *acc_out;
+    uint32_t *bits_out;  // packed sign bits instead of out (see Epilogue)
+    int out_words;
     int n, in_h, in_w, in_c, out_c, out_h, out_w, kh, kw, sh, sw, ph, pw;
     int cblocks;
 };
@@ -103,6 +105,21 @@ __global__ __launch_bounds__(256) void bwconv_kernel(BwArgs a)
         be = sum / (float)(a.kh * a.kw);
         if (cb == 0) a.beta_out[m] = be;
     }
+    if (a.bits_out) {
+        // channels 32*cb + [0, 32) are word cb of the pixel
+        static_assert(Q == 32, "one output word per lane");
+        uint32_t word = 0;
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const int co = cb * Q + q;
+            if (co >= a.out_c) break;
+            const float sc = a.scale ? a.scale[co] : a.scale_value;
+            const float bi = a.bias ? a.bias[co] : 0.0f;
+            if (sign_bit(epilogue_value(acc[q], sc, be, bi, a.relu))) word |= 1u << q;
+        }
+        store_through(&a.bits_out[m * a.out_words + cb], word);
+        return;
+    }
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
         const int co = cb * Q + q;
@@ -151,6 +168,8 @@ hipError_t launch_bwconv(const Geom &g, const Launch &L, const float *x, const f
     a.relu = e.relu;
     a.out = out;
     a.acc_out = acc_out;
+    a.bits_out = e.bits_out;
+    a.out_words = e.out_words;
     a.n = g.n;
     a.in_h = g.in_h;
     a.in_w = g.in_w;

@@ -75,6 +75,8 @@ struct MmaArgs {
     int relu;
     float *out;
     float *acc_out;
+    uint32_t *bits_out;  // packed sign bits instead of out (see Epilogue)
+    int out_words;
     int n, in_h, in_w, in_c, out_c, out_h, out_w, kh, kw, sh, sw, ph, pw;
     int chunks, ksteps, ntiles, mtiles, rows, cols, m_total;
     int x_bytes, out_bytes;
@@ -340,11 +342,29 @@ __global__ __launch_bounds__(kThreads) void bwmma_kernel(MmaArgs a)
         res[0] = acc[2] + red[2 * 64];
         res[1] = acc[3] + red[3 * 64];
     }
-    if (!live) return;
-
     // Epilogue: element r of block keep+u is pixel p_raw, channel
     // ntile*64 + 16*(keep+u) + 4*(lane/16) + r.
-    if (ntile == 0 && khalf == 0 && lane < 16 && a.a_pad) a.beta_out[pix] = be;
+    if (live && ntile == 0 && khalf == 0 && lane < 16 && a.a_pad) a.beta_out[pix] = be;
+    if (a.bits_out) {
+        // The wave's two blocks are channels 64*ntile + 16*keep + [0, 32): word
+        // 2*ntile + keep/2 of the pixel, element r of block keep+u at bit
+        // 16u + 4*(lane/16) + r; the four 16-lane groups OR their parts.
+        uint32_t part = 0;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int co = ntile * kChanTile + 16 * (keep + u) + 4 * (lane >> 4) + r;
+                const float y = epilogue_value(res[u][r], sc[u][r], be, bi[u][r], a.relu);
+                if (co < a.out_c && sign_bit(y)) part |= 1u << (16 * u + 4 * (lane >> 4) + r);
+            }
+        part |= __shfl_xor(part, 16);
+        part |= __shfl_xor(part, 32);
+        const int wi = 2 * ntile + keep / 2;
+        if (live && lane < 16 && wi < a.out_words) store_through(&a.bits_out[(long long)pix * a.out_words + wi], part);
+        return;
+    }
+    if (!live) return;
     const __amdgpu_buffer_rsrc_t orr = make_rsrc(a.acc_out ? (void *)a.acc_out : (void *)a.out, a.out_bytes);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -447,6 +467,8 @@ hipError_t launch_bwmma(const Geom &g, const Launch &L, const float *x, const fl
     a.relu = e.relu;
     a.out = out;
     a.acc_out = acc_out;
+    a.bits_out = e.bits_out;
+    a.out_words = e.out_words;
     a.n = g.n;
     a.in_h = g.in_h;
     a.in_w = g.in_w;

@@ -39,6 +39,8 @@ struct GArgs {
     int relu;
     float *out;
     int32_t *acc_out;
+    uint32_t *bits_out;     // packed sign bits instead of out (see Epilogue)
+    int out_words;
     int n, K, k4, out_c, tiles, mgroups, hw, in_c;
     int kbits;              // valid bits per row (H*W*Cin)
 };
@@ -129,9 +131,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void b
     __syncthreads();
     if (wave != 0) return;
     const int co = tile * kTile + lane;
-    if (co >= a.out_c) return;
-    const float sc = a.scale ? a.scale[co] : a.scale_value;
-    const float bi = a.bias ? a.bias[co] : 0.0f;
+    const bool co_ok = co < a.out_c;
+    if (!co_ok && !a.bits_out) return;  // the sign-bit path needs every lane
+    const float sc = a.scale ? (co_ok ? a.scale[co] : 0.0f) : a.scale_value;
+    const float bi = a.bias ? (co_ok ? a.bias[co] : 0.0f) : 0.0f;
 #pragma unroll
     for (int r = 0; r < kMR; ++r) {
         if (m0 + r >= a.n) break;
@@ -145,8 +148,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void b
             continue;
         }
         const float be = a.a_pad ? rbeta[r] : 1.0f;
-        float res = __builtin_fmaf((float)v * sc, be, bi);
-        if (a.relu) res = (res < 0.0f) ? 0.0f : res;
+        const float res = epilogue_value((float)v, sc, be, bi, a.relu);
+        if (a.bits_out) {
+            store_tile_bits(a.bits_out, m0 + r, a.out_words, (int)tile, co_ok && sign_bit(res));
+            continue;
+        }
         __hip_atomic_store(&a.out[o], res, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
@@ -217,6 +223,8 @@ hipError_t launch_gemm(const Geom &g, const Launch &L, int and_mode, const uint3
     a.relu = e.relu;
     a.out = out;
     a.acc_out = acc_out;
+    a.bits_out = e.bits_out;
+    a.out_words = e.out_words;
     a.n = g.n;
     a.K = g.kh * g.kw * g.words;
     a.k4 = (a.K + 3) / 4;

@@ -42,6 +42,30 @@ __device__ __forceinline__ void store_through(T *p, T v)
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// The fused epilogue's output value: neuron(v * scale * beta + bias).
+__device__ __forceinline__ float epilogue_value(float v, float sc, float be, float bi, int relu)
+{
+    const float r = __builtin_fmaf(v * sc, be, bi);
+    return relu ? ((r < 0.0f) ? 0.0f : r) : r;
+}
+
+// Sign bit of an output value, in the input encoding of the next binary
+// layer: 1 unless y < 0 (so +-0 and NaN give 1).
+__device__ __forceinline__ bool sign_bit(float y) { return !(y < 0.0f); }
+
+// Packed sign bits of one output pixel over a 64-channel tile held one
+// channel per lane (`bit` already 0 for channels past out_c).  Every lane of
+// the wave must call it.  Lanes 0 and 1 write words 2*tile and 2*tile + 1 of
+// the pixel's `out_words` words, where those exist.
+__device__ __forceinline__ void store_tile_bits(uint32_t *bits, long long pixel, int out_words, int tile, bool bit)
+{
+    const unsigned long long m = __ballot(bit);
+    const int lane = threadIdx.x & 63;
+    const int wi = 2 * tile + lane;
+    if (lane < 2 && wi < out_words)
+        store_through(&bits[pixel * out_words + wi], lane ? (uint32_t)(m >> 32) : (uint32_t)m);
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, int bytes)
 {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, bytes, kBufferFlags);
@@ -114,6 +138,11 @@ struct Epilogue {
     const float *a_pad;  // [n][bits_rows][bits_cols] or nullptr
     float *beta_out;     // [n][out_h][out_w] (used when a_pad is set)
     int relu;
+    // Packed sign bits of the output instead of fp32 values: [n][out_h][out_w]
+    // [out_words] words, channel c at bit c % 32 of word c / 32, bit = !(y < 0)
+    // for the value y the fp32 output would hold, bits past out_c zero.
+    uint32_t *bits_out;
+    int out_words;
 };
 
 // Launchers (each returns the hipGetLastError() of its launch).

@@ -32,6 +32,8 @@ struct XArgs {
     int relu;
     float *out;
     int32_t *acc_out;
+    uint32_t *bits_out;  // packed sign bits instead of out (see Epilogue)
+    int out_words;
     int n, in_h, in_w, in_c, out_c, out_h, out_w;
     int kh, kw, sh, sw, ph, pw, words;
     int rows, cols;  // padded extent (halo = pad)
@@ -270,7 +272,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void x
             v = a.in_c * valid - 2 * ((int)acc[p] - corr);
         }
         const float be = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(be_lane), p));
-        store_result_buf(a, orr, obase + (uint32_t)p * ostep, co, v, sc, bi, be);
+        if (a.bits_out)
+            store_tile_bits(a.bits_out, ((long long)img * a.out_h + oy) * a.out_w + ox, a.out_words, (int)tile,
+                            co_ok && sign_bit(epilogue_value((float)v, sc, be, bi, a.relu)));
+        else
+            store_result_buf(a, orr, obase + (uint32_t)p * ostep, co, v, sc, bi, be);
     }
 }
 
@@ -324,7 +330,10 @@ __global__ __launch_bounds__(256) void xconv_generic(XArgs a, int and_mode)
         be = sum / (float)(a.kh * a.kw);
         if (tile == 0 && lane == 0) a.beta_out[pix] = be;
     }
-    store_result(a, pix, co, v, sc, bi, be);
+    if (a.bits_out)
+        store_tile_bits(a.bits_out, pix, a.out_words, (int)tile, co_ok && sign_bit(epilogue_value((float)v, sc, be, bi, a.relu)));
+    else
+        store_result(a, pix, co, v, sc, bi, be);
 }
 
 template <int KH, int KW, int CW, int SW, int P>
@@ -411,6 +420,8 @@ XArgs make_args(const Geom &g, const uint32_t *bits, const LaneWeights &w, const
     a.relu = e.relu;
     a.out = out;
     a.acc_out = acc_out;
+    a.bits_out = e.bits_out;
+    a.out_words = e.out_words;
     a.n = g.n;
     a.in_h = g.in_h;
     a.in_w = g.in_w;

@@ -124,6 +124,56 @@ def window_abs_sum(layer: workloads.Layer, inputs: dict) -> np.ndarray:
     return s.numpy()[:, 0]
 
 
+def output_bound(layer: workloads.Layer, sub: dict, ref: dict) -> np.ndarray:
+    """The normwise fp32 bound on each final output (see the module doc)."""
+    oc = layer.out_c
+    scale = (sub["output_scale"].astype(np.float64) if sub.get("output_scale") is not None
+             else np.full(oc, layer.scale_value, np.float64))
+    bias = (sub["output_bias"].astype(np.float64) if sub.get("output_bias") is not None
+            else np.zeros(oc))
+    beta = ref["beta"][..., None]
+    if layer.type == "binary_weights":
+        S = window_abs_sum(layer, sub)[..., None]
+        return RTOL * (np.abs(scale * beta) * S + np.abs(bias)) + TINY
+    return RTOL * (np.abs(ref["acc"] * scale * beta) + np.abs(bias)) + TINY
+
+
+def unpack_words(words: np.ndarray, nbits: int) -> np.ndarray:
+    """uint32 words [..., W] -> bits [..., 32*W] (bit c%32 of word c//32), as uint8."""
+    w = np.ascontiguousarray(words).view("<u4")
+    b = np.unpackbits(w.view(np.uint8), axis=-1, bitorder="little")
+    return b[..., :nbits] if nbits is not None else b
+
+
+def compare_bits(layer: workloads.Layer, inputs: dict, words: np.ndarray, ref: dict = None, images=None):
+    """Packed sign bits of the output against the oracle: bit = !(y < 0).  The
+    sign is decided by the fp32 value, so positions whose oracle value lies
+    within the fp32 bound of 0 may take either bit; every other bit must match,
+    all of them under ReLU (its output is never below 0), and bits past out_c
+    must be 0."""
+    sub = inputs if images is None else slice_inputs(inputs, images)
+    if ref is None:
+        ref = oracle.bconv_layer(layer, sub)
+    g = words if images is None else words[images]
+    oc = layer.out_c
+    nw = (oc + 31) // 32
+    assert g.shape[-1] == nw, (g.shape, nw)
+    allbits = unpack_words(g, None)
+    assert not allbits[..., oc:].any(), f"{layer.name}: bits past out_c are set"
+    bits = allbits[..., :oc]
+    want = (~(ref["out"] < 0)).astype(np.uint8)
+    if layer.neuron == "relu":
+        certain = np.ones_like(want, dtype=bool)
+    else:
+        certain = np.abs(ref["out"]) > output_bound(layer, sub, ref)
+    bad = certain & (bits != want)
+    if bad.any():
+        i = tuple(np.argwhere(bad)[0])
+        raise AssertionError(f"{layer.name}: {int(bad.sum())} sign bits differ, first at {i}: "
+                             f"gpu {bits[i]} oracle value {ref['out'][i]}")
+    return int((~certain).sum())
+
+
 def compare(layer: workloads.Layer, inputs: dict, got: dict, ref: dict = None, images=None) -> dict:
     """Assert the GPU results (optionally only on `images`) match the oracle."""
     sub = inputs if images is None else slice_inputs(inputs, images)

@@ -233,6 +233,74 @@ def test_int8_mfma_path(dev, layer):
     parity.compare(layer, inputs, got, ref=ref)
 
 
+# ------------------------------------------------ packed sign-bit output
+
+def _bits_layers():
+    base = workloads.Layer("bits", "xnor", 2, 9, 10, 64, 70, 3, 3, 1, 1, 1, 1)
+    geoms = [
+        dict(name="bits_xnor_o70", use_beta=True, iscale_dist=("uniform", 0.5, 1.5), ibias_dist=("normal", 0.0, 0.2)),
+        dict(name="bits_xnor_o33", n=3, in_h=11, in_w=19, in_c=100, out_c=33),
+        dict(name="bits_and_o130", type="and", in_c=96, out_c=130, x_dist=("normal", 0.2, 1.0),
+             obias_dist=("normal", -20.0, 5.0)),
+        dict(name="bits_xnor_relu", out_c=128, neuron="relu"),
+        dict(name="bits_xnor_s2_o96", in_h=14, in_w=14, in_c=128, out_c=96, stride_h=2, stride_w=2),
+        dict(name="bits_fc_o66", n=5, in_h=4, in_w=5, in_c=37, out_c=66, kernel_h=4, kernel_w=5, pad_h=0, pad_w=0),
+        dict(name="bits_bw_o130", type="binary_weights", in_c=64, out_c=130, stride_h=2, stride_w=2),
+        dict(name="bits_bw_o40_beta", type="binary_weights", in_c=13, out_c=40, use_beta=True),
+        dict(name="bits_1px_o5", n=1, in_h=1, in_w=1, in_c=64, out_c=5),
+    ]
+    return [base.with_(**g) for g in geoms]
+
+
+BITS_LAYERS = _bits_layers()
+
+
+def _run_bits(layer, inputs, dev, generic=False, int8=False):
+    with parity.force_generic(generic):
+        conv = pca.BinaryConvolution.from_layer(layer, inputs, int8_mfma=int8)
+    try:
+        x = torch.from_numpy(inputs["x"]).to(dev)
+        words = conv.forward_bits(x).cpu().numpy()
+        out = conv.forward(x).cpu().numpy()
+        torch.cuda.synchronize()
+        return words, out, conv.main_kernel(x.shape[0])
+    finally:
+        conv.close()
+
+
+@pytest.mark.parametrize("layer", BITS_LAYERS, ids=[l.name for l in BITS_LAYERS])
+def test_forward_bits(dev, layer):
+    """bconv_forward_bits: the sign bits of the fp32 output, packed for the next
+    binary layer, on the specialised and generic kernels (and the int8 path for
+    XNOR / AND); exactly the signs of the same kernel's fp32 output, and the
+    oracle's signs wherever fp32 rounding cannot decide them."""
+    inputs = workloads.make_inputs(layer, 8000 + BITS_LAYERS.index(layer))
+    _log(f"bits {layer}")
+    ref = oracle.bconv_layer(layer, inputs)
+    variants = [dict(generic=False), dict(generic=True)]
+    if layer.type != "binary_weights":
+        variants.append(dict(int8=True))
+    for v in variants:
+        words, out, kernel = _run_bits(layer, inputs, dev, **v)
+        bits = parity.unpack_words(words, layer.out_c)
+        assert np.array_equal(bits, (~(out < 0)).astype(np.uint8)), f"{kernel}: bits differ from its fp32 signs"
+        parity.compare_bits(layer, inputs, words, ref=ref)
+
+
+@pytest.mark.parametrize("index", range(len(workloads.LAYERS)), ids=[l.name for l in workloads.LAYERS])
+def test_forward_bits_measured_layer(dev, index):
+    """Sign bits on each measured layer at full size (oracle on sampled images)."""
+    layer = workloads.LAYERS[index]
+    inputs = workloads.make_inputs(layer, workloads.layer_seed(index))
+    _log(f"bits layer {layer.name}")
+    words, out, kernel = _run_bits(layer, inputs, dev)
+    bits = parity.unpack_words(words, layer.out_c)
+    assert np.array_equal(bits, (~(out < 0)).astype(np.uint8)), f"{kernel}: bits differ from its fp32 signs"
+    n = layer.n
+    images = sorted({0, 1, n - 1}) if layer.is_fc else sorted({0, n - 1})
+    parity.compare_bits(layer, inputs, words, images=np.array(images))
+
+
 # ------------------------------------------------------------ robustness
 
 def test_repeat_is_bit_identical(dev):
