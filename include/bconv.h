@@ -27,10 +27,13 @@
  *     input channel f is bit (f % 32) of word (f / 32).  Bit 1 is +1 (XNOR,
  *     binaryWeights) or 1 (AND); bit 0 is -1 or 0.  Bits at positions >= in_c
  *     in the last word are ignored.
- *   - Geometry: out_h = (in_h + 2*pad_h - kernel_h)/stride_h + 1 (likewise w);
- *     tap ky of output y reads input row y*stride_h - pad_h + ky.  With an odd
- *     kernel, pad = kernel/2 and stride 1 this is the page's centred window
- *     [-k/2, (k-1)/2].  Taps outside the image contribute nothing.
+ *   - Geometry: out_h = (in_h + pad_h + pad_h_end - kernel_h)/stride_h + 1
+ *     (likewise w), with pad_h the leading (top) and pad_h_end the trailing
+ *     (bottom) zero padding; tap ky of output y reads input row
+ *     y*stride_h - pad_h + ky.  pad = kernel/2, pad_end = (kernel-1)/2 and
+ *     stride 1 give the page's centred window [-k/2, (k-1)/2] (the beta
+ *     paragraph), for even kernels as well as odd ones.  Taps outside the
+ *     image contribute nothing.
  *   - in' = fmaf(in, input_scale[f], input_bias[f]) in fp32; the sign is
  *     taken as (in' < 0) ? -1 : +1 (so -0 and NaN binarise to +1);
  *     subnormals are kept.
@@ -105,12 +108,15 @@ typedef enum {
 typedef struct {
     int32_t in_h, in_w, in_c; /* source image height, width, feature channels (>= 1) */
     int32_t out_c;            /* output feature channels (>= 1) */
-    int32_t kernel_h, kernel_w; /* >= 1; kernel_h <= in_h + 2*pad_h, likewise w */
+    int32_t kernel_h, kernel_w; /* >= 1; kernel_h <= in_h + pad_h + pad_h_end, likewise w */
     int32_t stride_h, stride_w; /* >= 1 */
-    int32_t pad_h, pad_w;     /* leading = trailing zero padding, 0 <= pad < kernel */
+    int32_t pad_h, pad_w;     /* leading (top, left) zero padding, 0 <= pad < kernel */
     int32_t groups;           /* must be 1 (MPSCNNBinaryConvolution, groups note) */
     int32_t neuron;           /* bconv_neuron_t */
     float scale_value;        /* output scale used when output_scale is NULL */
+    int32_t pad_h_end, pad_w_end; /* trailing (bottom, right) zero padding,
+                                     0 <= pad_end < kernel; equal to pad_h / pad_w
+                                     for the usual symmetric padding */
 } bconv_desc_t;
 
 /* Where the per-step intermediates sit in a forward call's workspace, for

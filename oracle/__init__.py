@@ -49,9 +49,11 @@ def load(path: Optional[str] = None):
     lib = ctypes.CDLL(p)
     i, f, vp = ctypes.c_int, ctypes.c_float, ctypes.c_void_p
     lib.oracle_bconv.restype = i
-    lib.oracle_bconv.argtypes = [i] * 14 + [f] + [vp] * 12 + [i]
+    lib.oracle_bconv.argtypes = [i] * 16 + [f] + [vp] * 12 + [i]
     lib.oracle_out_dim.restype = i
     lib.oracle_out_dim.argtypes = [i, i, i, i]
+    lib.oracle_out_dim2.restype = i
+    lib.oracle_out_dim2.argtypes = [i, i, i, i, i]
     if path is None:
         _lib = lib
     return lib
@@ -61,18 +63,21 @@ def _ptr(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
 
-def out_dim(size: int, kernel: int, stride: int, pad: int) -> int:
-    return load().oracle_out_dim(size, kernel, stride, pad)
+def out_dim(size: int, kernel: int, stride: int, pad: int, pad_end: Optional[int] = None) -> int:
+    """Output extent for leading padding `pad` and trailing `pad_end` (= pad when omitted)."""
+    return load().oracle_out_dim2(size, kernel, stride, pad, pad if pad_end is None else pad_end)
 
 
 def bconv(x: np.ndarray, weight_bits: np.ndarray, *, type: str, out_c: int,
-          kernel=(1, 1), stride=(1, 1), pad=(0, 0), output_scale=None, output_bias=None,
+          kernel=(1, 1), stride=(1, 1), pad=(0, 0), pad_end=None, output_scale=None, output_bias=None,
           input_scale=None, input_bias=None, use_beta: bool = False, neuron: str = "none",
           scale_value: float = 1.0, threads: int = 0, want=("out", "acc", "beta", "a_map", "signs"),
           lib=None) -> dict:
     """Evaluate binary convolution on the CPU.
 
     ``x`` is float32 NHWC, ``weight_bits`` uint32 ``[out_c][kh][kw][ceil(Cin/32)]``.
+    ``pad`` is the leading (top, left) zero padding and ``pad_end`` the
+    trailing (bottom, right) one, equal to ``pad`` when omitted.
     Returns a dict of float64 ``out``, the pre-epilogue sum ``acc`` (int32 for
     XNOR/AND, float64 for binary_weights), ``beta`` [n,oh,ow], ``a_map``
     [n,h,w] (with ``use_beta``) and the binarised input ``signs`` (int8).
@@ -84,11 +89,12 @@ def bconv(x: np.ndarray, weight_bits: np.ndarray, *, type: str, out_c: int,
     kh, kw = kernel
     sh, sw = stride
     ph, pw = pad
+    phe, pwe = pad if pad_end is None else pad_end
     words = (c + 31) // 32
     if weight_bits.shape != (out_c, kh, kw, words):
         raise ValueError(f"weight_bits shape {weight_bits.shape} != {(out_c, kh, kw, words)}")
-    oh = lib.oracle_out_dim(h, kh, sh, ph)
-    ow = lib.oracle_out_dim(w, kw, sw, pw)
+    oh = lib.oracle_out_dim2(h, kh, sh, ph, phe)
+    ow = lib.oracle_out_dim2(w, kw, sw, pw, pwe)
     if oh <= 0 or ow <= 0:
         raise ValueError("kernel larger than the padded input")
 
@@ -104,7 +110,7 @@ def bconv(x: np.ndarray, weight_bits: np.ndarray, *, type: str, out_c: int,
     signs = np.empty((n, h, w, c), np.int8) if ("signs" in want and t != 0) else None
     a_map = np.empty((n, h, w), np.float64) if ("a_map" in want and use_beta) else None
     beta = np.empty((n, oh, ow), np.float64) if "beta" in want else None
-    rc = lib.oracle_bconv(n, h, w, c, out_c, kh, kw, sh, sw, ph, pw, t, int(bool(use_beta)),
+    rc = lib.oracle_bconv(n, h, w, c, out_c, kh, kw, sh, sw, ph, pw, phe, pwe, t, int(bool(use_beta)),
                           NEURON_CODES[neuron], float(scale_value), _ptr(x), _ptr(weight_bits),
                           _ptr(output_scale), _ptr(output_bias), _ptr(input_scale),
                           _ptr(input_bias), _ptr(out), _ptr(acc_i), _ptr(acc_r), _ptr(signs),
@@ -119,7 +125,8 @@ def bconv_layer(layer, inputs: dict, threads: int = 0, lib=None, **kw) -> dict:
     """``bconv`` on a ``workloads.Layer`` and the arrays ``make_inputs`` drew."""
     return bconv(inputs["x"], inputs["weight_bits"], type=layer.type, out_c=layer.out_c,
                  kernel=(layer.kernel_h, layer.kernel_w), stride=(layer.stride_h, layer.stride_w),
-                 pad=(layer.pad_h, layer.pad_w), output_scale=inputs.get("output_scale"),
+                 pad=(layer.pad_h, layer.pad_w), pad_end=(layer.pad_h_end, layer.pad_w_end),
+                 output_scale=inputs.get("output_scale"),
                  output_bias=inputs.get("output_bias"), input_scale=inputs.get("input_scale"),
                  input_bias=inputs.get("input_bias"), use_beta=layer.use_beta,
                  neuron=layer.neuron, scale_value=layer.scale_value, threads=threads, lib=lib, **kw)

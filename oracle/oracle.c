@@ -16,7 +16,10 @@
  * test against something other than this file):
  *  - layout NHWC fp32; weights are uint32 words [Cout][kh][kw][ceil(Cin/32)]
  *    with channel c at bit c%32 of word c/32 (the pages only say "32-bit words").
- *  - geometry: ih = oh*stride - pad + ky, out = (in + 2*pad - k)/stride + 1.
+ *  - geometry: ih = oh*stride - pad + ky, out = (in + pad + pad_end - k)/stride + 1,
+ *    with pad the leading and pad_end the trailing zero padding (equal for the
+ *    odd kernels; the pages' centred window [-k/2, (k-1)/2] of the beta
+ *    paragraph gives an even kernel pad = k/2 and pad_end = k/2 - 1).
  *  - padded taps contribute nothing to the sum.
  *  - input affine x' = fmaf(x, inputScale[c], inputBias[c]) in fp32, applied
  *    before the sign and before the A map.
@@ -43,11 +46,13 @@
 #define ORACLE_NEURON_NONE 0
 #define ORACLE_NEURON_RELU 1
 
-int oracle_out_dim(int in, int k, int stride, int pad)
+int oracle_out_dim2(int in, int k, int stride, int pad, int pad_end)
 {
-    if (stride <= 0 || k <= 0 || in + 2 * pad < k) return 0;
-    return (in + 2 * pad - k) / stride + 1;
+    if (stride <= 0 || k <= 0 || in + pad + pad_end < k) return 0;
+    return (in + pad + pad_end - k) / stride + 1;
 }
+
+int oracle_out_dim(int in, int k, int stride, int pad) { return oracle_out_dim2(in, k, stride, pad, pad); }
 
 /*
  * Input pre-offset and scale (MPSCNNBinaryConvolution, Overview, paragraph on
@@ -113,21 +118,23 @@ static int input_sign(float v, int type)
  * Returns 0, or -1 on an argument the method does not define.
  */
 int oracle_bconv(int n, int in_h, int in_w, int in_c, int out_c, int kernel_h, int kernel_w,
-                 int stride_h, int stride_w, int pad_h, int pad_w, int type, int use_beta,
+                 int stride_h, int stride_w, int pad_h, int pad_w, int pad_h_end, int pad_w_end,
+                 int type, int use_beta,
                  int neuron, float scale_value, const float *x, const uint32_t *weight_bits,
                  const float *output_scale, const float *output_bias, const float *input_scale,
                  const float *input_bias, double *out, int32_t *acc_int, double *acc_real,
                  int8_t *signs, double *a_map, double *beta, int n_threads)
 {
     if (n < 0 || in_h <= 0 || in_w <= 0 || in_c <= 0 || out_c <= 0 || kernel_h <= 0 ||
-        kernel_w <= 0 || stride_h <= 0 || stride_w <= 0 || pad_h < 0 || pad_w < 0)
+        kernel_w <= 0 || stride_h <= 0 || stride_w <= 0 || pad_h < 0 || pad_w < 0 || pad_h_end < 0 ||
+        pad_w_end < 0)
         return -1;
     if (type != ORACLE_BINARY_WEIGHTS && type != ORACLE_XNOR && type != ORACLE_AND) return -1;
     if (neuron != ORACLE_NEURON_NONE && neuron != ORACLE_NEURON_RELU) return -1;
     if (!x || !weight_bits || !out) return -1;
 
-    const int out_h = oracle_out_dim(in_h, kernel_h, stride_h, pad_h);
-    const int out_w = oracle_out_dim(in_w, kernel_w, stride_w, pad_w);
+    const int out_h = oracle_out_dim2(in_h, kernel_h, stride_h, pad_h, pad_h_end);
+    const int out_w = oracle_out_dim2(in_w, kernel_w, stride_w, pad_w, pad_w_end);
     if (out_h <= 0 || out_w <= 0) return -1;
     const int words = (in_c + 31) / 32;
     const long in_pixels = (long)n * in_h * in_w;

@@ -35,12 +35,13 @@ class BinaryConvolution:
     """
 
     def __init__(self, *, in_h: int, in_w: int, in_c: int, out_c: int, kernel: tuple,
-                 stride: tuple = (1, 1), pad: tuple = (0, 0), type: str = "xnor",
+                 stride: tuple = (1, 1), pad: tuple = (0, 0), pad_end=None, type: str = "xnor",
                  weight_bits: np.ndarray, output_scale=None, output_bias=None,
                  input_scale=None, input_bias=None, use_beta: bool = False,
                  neuron: str = "none", scale_value: float = 1.0, int8_mfma: bool = False):
+        pe = pad if pad_end is None else pad_end
         self.desc = make_desc(in_h, in_w, in_c, out_c, kernel[0], kernel[1], stride[0], stride[1],
-                              pad[0], pad[1], 1, NEURON_CODES[neuron], scale_value)
+                              pad[0], pad[1], 1, NEURON_CODES[neuron], scale_value, pe[0], pe[1])
         self.type = TYPE_CODES[type]
         self.flags = (BCONV_FLAG_USE_BETA_SCALING if use_beta else BCONV_FLAG_NONE) | \
             (BCONV_FLAG_INT8_MFMA if int8_mfma else BCONV_FLAG_NONE)
@@ -54,7 +55,8 @@ class BinaryConvolution:
         (``int8_mfma``: the int8 matrix-core comparison path)."""
         return cls(in_h=layer.in_h, in_w=layer.in_w, in_c=layer.in_c, out_c=layer.out_c,
                    kernel=(layer.kernel_h, layer.kernel_w), stride=(layer.stride_h, layer.stride_w),
-                   pad=(layer.pad_h, layer.pad_w), type=layer.type,
+                   pad=(layer.pad_h, layer.pad_w), pad_end=(layer.pad_h_end, layer.pad_w_end),
+                   type=layer.type,
                    weight_bits=inputs["weight_bits"], output_scale=inputs.get("output_scale"),
                    output_bias=inputs.get("output_bias"), input_scale=inputs.get("input_scale"),
                    input_bias=inputs.get("input_bias"), use_beta=layer.use_beta,

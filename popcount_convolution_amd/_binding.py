@@ -54,7 +54,8 @@ class BconvError(RuntimeError):
 class bconv_desc_t(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "in_h", "in_w", "in_c", "out_c", "kernel_h", "kernel_w", "stride_h", "stride_w",
-        "pad_h", "pad_w", "groups", "neuron")] + [("scale_value", ctypes.c_float)]
+        "pad_h", "pad_w", "groups", "neuron")] + [("scale_value", ctypes.c_float)] + \
+        [("pad_h_end", ctypes.c_int32), ("pad_w_end", ctypes.c_int32)]
 
 
 class bconv_workspace_layout_t(ctypes.Structure):
@@ -139,9 +140,12 @@ def _ptr(x) -> Optional[int]:
 
 
 def make_desc(in_h, in_w, in_c, out_c, kernel_h, kernel_w, stride_h=1, stride_w=1, pad_h=0,
-              pad_w=0, groups=1, neuron=BCONV_NEURON_NONE, scale_value=1.0) -> bconv_desc_t:
+              pad_w=0, groups=1, neuron=BCONV_NEURON_NONE, scale_value=1.0, pad_h_end=None,
+              pad_w_end=None) -> bconv_desc_t:
+    """Trailing padding defaults to the leading one (symmetric padding)."""
     return bconv_desc_t(in_h, in_w, in_c, out_c, kernel_h, kernel_w, stride_h, stride_w, pad_h,
-                        pad_w, groups, neuron, scale_value)
+                        pad_w, groups, neuron, scale_value, pad_h if pad_h_end is None else pad_h_end,
+                        pad_w if pad_w_end is None else pad_w_end)
 
 
 def bconv_validate_desc(desc: bconv_desc_t, type: int, flags: int) -> int:

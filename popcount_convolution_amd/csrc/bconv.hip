@@ -62,7 +62,8 @@ constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
-int out_dim(int in, int k, int s, int p) { return (in + 2 * p - k) / s + 1; }
+// Output extent for leading padding p and trailing padding pe.
+int out_dim(int in, int k, int s, int p, int pe) { return (in + p + pe - k) / s + 1; }
 
 bconv_status_t check_desc(const bconv_desc_t *d, int32_t type, uint32_t flags)
 {
@@ -85,9 +86,10 @@ bconv_status_t check_desc(const bconv_desc_t *d, int32_t type, uint32_t flags)
         return fail(BCONV_ERR_INVALID_ARGUMENT, "kernel extents must be >= 1");
     if (d->stride_h < 1 || d->stride_w < 1 || d->stride_h > kMaxExtent || d->stride_w > kMaxExtent)
         return fail(BCONV_ERR_INVALID_ARGUMENT, "strides must be >= 1");
-    if (d->pad_h < 0 || d->pad_w < 0 || d->pad_h >= d->kernel_h || d->pad_w >= d->kernel_w)
+    if (d->pad_h < 0 || d->pad_w < 0 || d->pad_h >= d->kernel_h || d->pad_w >= d->kernel_w ||
+        d->pad_h_end < 0 || d->pad_w_end < 0 || d->pad_h_end >= d->kernel_h || d->pad_w_end >= d->kernel_w)
         return fail(BCONV_ERR_INVALID_ARGUMENT, "padding must satisfy 0 <= pad < kernel");
-    if (d->in_h + 2 * d->pad_h < d->kernel_h || d->in_w + 2 * d->pad_w < d->kernel_w)
+    if (d->in_h + d->pad_h + d->pad_h_end < d->kernel_h || d->in_w + d->pad_w + d->pad_w_end < d->kernel_w)
         return fail(BCONV_ERR_INVALID_ARGUMENT, "kernel larger than the padded input");
     if ((long long)d->in_c * d->kernel_h * d->kernel_w > kMaxWindowBits)
         return fail(BCONV_ERR_INVALID_ARGUMENT, "in_c*kernel_h*kernel_w exceeds 2^24");
@@ -116,8 +118,8 @@ bconv::Geom make_geom(const bconv_handle *h, int n)
     g.simds = h->simds;
     g.bits_halo_h = d.pad_h;
     g.bits_halo_w = d.pad_w;
-    g.bits_rows = d.in_h + 2 * d.pad_h;
-    g.bits_cols = d.in_w + 2 * d.pad_w;
+    g.bits_rows = d.in_h + d.pad_h + d.pad_h_end;
+    g.bits_cols = d.in_w + d.pad_w + d.pad_w_end;
     // A strip of the specialised kernel may read past the last column of the
     // last row; those words exist and are zero.
     g.bits_slack_words = (long long)(8 * g.sw + g.kw) * g.words + 64;
@@ -321,8 +323,8 @@ bconv_status_t bconv_create(const bconv_desc_t *desc, const uint32_t *weight_bit
     h->desc = *desc;
     h->type = type;
     h->flags = flags;
-    h->out_h = out_dim(desc->in_h, desc->kernel_h, desc->stride_h, desc->pad_h);
-    h->out_w = out_dim(desc->in_w, desc->kernel_w, desc->stride_w, desc->pad_w);
+    h->out_h = out_dim(desc->in_h, desc->kernel_h, desc->stride_h, desc->pad_h, desc->pad_h_end);
+    h->out_w = out_dim(desc->in_w, desc->kernel_w, desc->stride_w, desc->pad_w, desc->pad_w_end);
     h->words = (desc->in_c + 31) / 32;
     h->tiles = (desc->out_c + bconv::kTile - 1) / bconv::kTile;
     const char *fg = getenv("BCONV_FORCE_GENERIC");
@@ -419,7 +421,7 @@ bconv_status_t bconv_create_fc(int32_t in_h, int32_t in_w, int32_t in_c, int32_t
     d.kernel_h = in_h;
     d.kernel_w = in_w;
     d.stride_h = d.stride_w = 1;
-    d.pad_h = d.pad_w = 0;
+    d.pad_h = d.pad_w = d.pad_h_end = d.pad_w_end = 0;
     d.groups = 1;
     d.neuron = neuron;
     d.scale_value = scale_value;

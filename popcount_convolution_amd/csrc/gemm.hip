@@ -185,7 +185,8 @@ __global__ void prepack_flat_kernel(const uint32_t *__restrict__ user, uint32_t 
 
 bool gemm_route(const Geom &g)
 {
-    return g.kh == g.in_h && g.kw == g.in_w && g.sh == 1 && g.sw == 1 && g.ph == 0 && g.pw == 0;
+    return g.kh == g.in_h && g.kw == g.in_w && g.sh == 1 && g.sw == 1 && g.ph == 0 && g.pw == 0 &&
+           g.bits_rows == g.in_h && g.bits_cols == g.in_w;  // no trailing padding either
 }
 
 size_t gemm_weight_words(const Geom &g)

@@ -386,6 +386,10 @@ const FastEntry kFast[] = {
     BCONV_FAST_P(1, 1, 1, 1), BCONV_FAST_P(1, 1, 2, 1), BCONV_FAST_P(1, 1, 4, 1),
     BCONV_FAST_P(1, 1, 8, 1),
     BCONV_FAST_P(5, 5, 1, 1), BCONV_FAST_P(5, 5, 2, 1),
+    // even kernels (the centred window of an even kernel pads k/2 before and
+    // k/2 - 1 after)
+    BCONV_FAST_P(2, 2, 1, 1), BCONV_FAST_P(2, 2, 2, 1), BCONV_FAST_P(2, 2, 4, 1),
+    BCONV_FAST_P(4, 4, 1, 1), BCONV_FAST_P(4, 4, 2, 1),
 };
 #undef BCONV_FAST_P
 #undef BCONV_FAST

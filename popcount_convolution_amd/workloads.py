@@ -54,14 +54,25 @@ class Layer:
     iscale_dist: Optional[tuple] = None
     ibias_dist: Optional[tuple] = None
     scale_value: float = 1.0
+    # trailing (bottom / right) zero padding; None = the leading one
+    pad_bottom: Optional[int] = None
+    pad_right: Optional[int] = None
+
+    @property
+    def pad_h_end(self) -> int:
+        return self.pad_h if self.pad_bottom is None else self.pad_bottom
+
+    @property
+    def pad_w_end(self) -> int:
+        return self.pad_w if self.pad_right is None else self.pad_right
 
     @property
     def out_h(self) -> int:
-        return (self.in_h + 2 * self.pad_h - self.kernel_h) // self.stride_h + 1
+        return (self.in_h + self.pad_h + self.pad_h_end - self.kernel_h) // self.stride_h + 1
 
     @property
     def out_w(self) -> int:
-        return (self.in_w + 2 * self.pad_w - self.kernel_w) // self.stride_w + 1
+        return (self.in_w + self.pad_w + self.pad_w_end - self.kernel_w) // self.stride_w + 1
 
     @property
     def words(self) -> int:
@@ -71,7 +82,7 @@ class Layer:
     def is_fc(self) -> bool:
         return (self.kernel_h == self.in_h and self.kernel_w == self.in_w
                 and self.stride_h == 1 and self.stride_w == 1
-                and self.pad_h == 0 and self.pad_w == 0)
+                and self.pad_h == 0 and self.pad_w == 0 and self.pad_h_end == 0 and self.pad_w_end == 0)
 
     def nominal_macs(self, n: Optional[int] = None) -> int:
         """N*Ho*Wo*Cout*kh*kw*Cin: padded taps counted (bit-MACs, or fp32 MACs

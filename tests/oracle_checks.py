@@ -51,6 +51,16 @@ def conv2d_ref(values_nhwc: np.ndarray, weights_okkc: np.ndarray, stride, pad) -
     return y.numpy().transpose(0, 2, 3, 1)
 
 
+def conv2d_ref_pad(values_nhwc: np.ndarray, weights_okkc: np.ndarray, stride, pad, pad_end) -> np.ndarray:
+    """float64 torch conv2d after explicit zero padding: `pad` rows / columns
+    before (top, left) and `pad_end` after (bottom, right); NHWC in and out."""
+    xt = torch.from_numpy(np.ascontiguousarray(values_nhwc.transpose(0, 3, 1, 2)))
+    xt = torch.nn.functional.pad(xt, (pad[1], pad_end[1], pad[0], pad_end[0]))
+    wt = torch.from_numpy(np.ascontiguousarray(weights_okkc.transpose(0, 3, 1, 2)))
+    y = torch.nn.functional.conv2d(xt, wt, stride=tuple(stride))
+    return y.numpy().transpose(0, 2, 3, 1)
+
+
 def _run(lib, x, wbits, form, out_c, k=(1, 1), s=(1, 1), p=(0, 0), **kw):
     return oracle.bconv(x, wbits, type=form, out_c=out_c, kernel=k, stride=s, pad=p, lib=lib,
                         threads=1, **kw)
@@ -186,6 +196,26 @@ def check_beta_window(lib):
                 assert acc[0, y, y, 0] == (1.0 if inside else 0.0), (k, pos, y)
 
 
+def check_centred_window_any_kernel(lib):
+    """The beta equation's window [-k/2, (k-1)/2] as leading padding k/2 and
+    trailing padding (k-1)/2, stride 1: the output keeps the input size for
+    even kernels as for odd ones, and output y sees exactly input rows
+    y + first .. y + last of the fixture."""
+    for row in _rows("beta_window.txt"):
+        k, first, last = int(row[0]), int(row[1]), int(row[2])
+        size = 9
+        wb = np.full((1, k, k, 1), 1, np.uint32)
+        for pos in range(size):
+            x = np.zeros((1, size, size, 1), np.float32)
+            x[0, pos, pos, 0] = 1.0
+            acc = _run(lib, x, wb, "binary_weights", 1, k=(k, k), p=(k // 2, k // 2),
+                       pad_end=((k - 1) // 2, (k - 1) // 2))["acc"]
+            assert acc.shape[1:3] == (size, size), (k, acc.shape)
+            for y in range(size):
+                inside = first <= pos - y <= last
+                assert acc[0, y, y, 0] == (1.0 if inside else 0.0), (k, pos, y)
+
+
 # ----------------------------------------------------------- textbook routines
 
 def check_bruteforce_conv(lib):
@@ -205,6 +235,34 @@ def check_bruteforce_conv(lib):
             want = conv2d_ref(xv, bits_to_values(wb, c, form), (sh, sw), (ph, pw))
             assert got.shape == want.shape
             assert np.array_equal(got, np.rint(want).astype(np.int64)), (form, n, h, w, c)
+
+
+def check_bruteforce_asymmetric_padding(lib):
+    """Different leading and trailing padding (even kernels, and odd ones):
+    XNOR / AND sums equal a float64 conv2d of the binarised input after
+    explicit zero padding, binaryWeights sums its full-precision conv2d, and
+    beta the box sum of the A map over the same padded window / (kh*kw)."""
+    rng = _rng(15)
+    cases = [(2, 6, 7, 33, 5, 2, 2, 1, 1, 1, 1, 0, 0), (1, 9, 8, 64, 3, 4, 4, 1, 1, 2, 2, 1, 1),
+             (1, 7, 9, 40, 4, 4, 2, 2, 1, 2, 1, 1, 0), (2, 5, 6, 17, 3, 3, 3, 1, 2, 0, 1, 2, 2),
+             (1, 8, 8, 100, 2, 6, 6, 1, 1, 3, 3, 2, 2), (1, 4, 5, 3, 2, 2, 3, 1, 1, 0, 2, 1, 0)]
+    for (n, h, w, c, o, kh, kw, sh, sw, ph, pw, phe, pwe) in cases:
+        x = rng.normal(size=(n, h, w, c)).astype(np.float32)
+        x[rng.random(x.shape) < 0.05] = 0.0
+        wb = _rand_bits(rng, (o, kh, kw, (c + 31) // 32))
+        geo = dict(k=(kh, kw), s=(sh, sw), p=(ph, pw), pad_end=(phe, pwe))
+        for form in ("xnor", "and"):
+            got = _run(lib, x, wb, form, o, **geo)["acc"]
+            xv = np.where(x < 0, -1.0 if form == "xnor" else 0.0, 1.0)
+            want = conv2d_ref_pad(xv, bits_to_values(wb, c, form), (sh, sw), (ph, pw), (phe, pwe))
+            assert got.shape == want.shape, (got.shape, want.shape)
+            assert np.array_equal(got, np.rint(want).astype(np.int64)), (form, kh, kw, ph, phe)
+        r = _run(lib, x, wb, "binary_weights", o, use_beta=True, **geo)
+        want = conv2d_ref_pad(x.astype(np.float64), bits_to_values(wb, c, "xnor"), (sh, sw), (ph, pw), (phe, pwe))
+        np.testing.assert_allclose(r["acc"], want, rtol=0, atol=1e-12)
+        a = np.abs(x.astype(np.float64)).sum(axis=-1, keepdims=True) / c
+        box = conv2d_ref_pad(a, np.ones((1, kh, kw, 1)), (sh, sw), (ph, pw), (phe, pwe))[..., 0] / (kh * kw)
+        np.testing.assert_allclose(r["beta"], box, rtol=1e-12, atol=0)
 
 
 def check_binary_weights_conv(lib):
@@ -414,7 +472,8 @@ def check_accumulator_parity_and_range(lib):
 
 ALL_CHECKS = [
     check_truth_table, check_word_identities, check_word_ranges, check_fc_conditions_and_matmul,
-    check_fc_equals_centred_conv, check_beta_window, check_bruteforce_conv,
+    check_fc_equals_centred_conv, check_beta_window, check_centred_window_any_kernel, check_bruteforce_conv,
+    check_bruteforce_asymmetric_padding,
     check_binary_weights_conv, check_all_ones_closed_form, check_beta_constant_input,
     check_a_map_definition, check_epilogue_closed_form, check_sign_under_affine,
     check_tail_bits_ignored, check_degenerate_single_channel,

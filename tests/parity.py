@@ -117,10 +117,10 @@ def window_abs_sum(layer: workloads.Layer, inputs: dict) -> np.ndarray:
         x = x * inputs["input_scale"].astype(np.float64)
     if inputs.get("input_bias") is not None:
         x = x + inputs["input_bias"].astype(np.float64)
-    a = np.abs(x).sum(axis=-1)[:, None]
+    a = torch.from_numpy(np.abs(x).sum(axis=-1)[:, None])
+    a = torch.nn.functional.pad(a, (layer.pad_w, layer.pad_w_end, layer.pad_h, layer.pad_h_end))
     k = torch.ones((1, 1, layer.kernel_h, layer.kernel_w), dtype=torch.float64)
-    s = torch.nn.functional.conv2d(torch.from_numpy(a), k, stride=(layer.stride_h, layer.stride_w),
-                                   padding=(layer.pad_h, layer.pad_w))
+    s = torch.nn.functional.conv2d(a, k, stride=(layer.stride_h, layer.stride_w))
     return s.numpy()[:, 0]
 
 

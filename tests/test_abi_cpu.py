@@ -64,6 +64,10 @@ def _desc(**kw):
     (dict(out_c=0), pca.BCONV_XNOR, 0, pca.BCONV_ERR_INVALID_ARGUMENT),
     (dict(stride_w=0), pca.BCONV_XNOR, 0, pca.BCONV_ERR_INVALID_ARGUMENT),
     (dict(pad_h=3), pca.BCONV_XNOR, 0, pca.BCONV_ERR_INVALID_ARGUMENT),
+    (dict(kernel_h=2, kernel_w=4, pad_h=1, pad_w=2, pad_h_end=0, pad_w_end=1), pca.BCONV_XNOR, 0,
+     pca.BCONV_OK),  # centred even kernels
+    (dict(pad_h_end=3), pca.BCONV_XNOR, 0, pca.BCONV_ERR_INVALID_ARGUMENT),
+    (dict(pad_w_end=-1), pca.BCONV_XNOR, 0, pca.BCONV_ERR_INVALID_ARGUMENT),
     (dict(pad_w=-1), pca.BCONV_XNOR, 0, pca.BCONV_ERR_INVALID_ARGUMENT),
     (dict(kernel_h=11, pad_h=1), pca.BCONV_XNOR, 0, pca.BCONV_ERR_INVALID_ARGUMENT),
     (dict(in_c=1 << 20, kernel_h=5, kernel_w=5, pad_h=0, pad_w=0), pca.BCONV_XNOR, 0,

@@ -182,6 +182,51 @@ def test_binary_weights_special_values(dev):
         assert np.any(g[1] != 0) and np.any(g[2] != 0), "tiny values must not flush to zero"
 
 
+# ------------------------------------------------ asymmetric padding
+
+def _pad_layers():
+    base = workloads.Layer("pad", "xnor", 2, 9, 11, 64, 70, 3, 3, 1, 1, 1, 1)
+    geoms = [
+        dict(name="pad_k2_centred", kernel_h=2, kernel_w=2, pad_h=1, pad_w=1, pad_bottom=0, pad_right=0),
+        dict(name="pad_k4_centred_beta", kernel_h=4, kernel_w=4, pad_h=2, pad_w=2, pad_bottom=1, pad_right=1,
+             use_beta=True, iscale_dist=("uniform", 0.5, 1.5), ibias_dist=("normal", 0.0, 0.2)),
+        dict(name="pad_k4_and_cw2", type="and", in_c=50, kernel_h=4, kernel_w=4, pad_h=2, pad_w=2,
+             pad_bottom=1, pad_right=1, x_dist=("normal", 0.2, 1.0)),
+        dict(name="pad_k2_cw4", in_c=128, out_c=130, kernel_h=2, kernel_w=2, pad_h=1, pad_w=1, pad_bottom=0,
+             pad_right=0, n=3, in_h=14, in_w=15),
+        dict(name="pad_k3_top_only", pad_h=2, pad_w=0, pad_bottom=0, pad_right=2),
+        dict(name="pad_k3_s2_asym", in_c=96, stride_h=2, stride_w=2, pad_h=0, pad_w=1, pad_bottom=2, pad_right=0),
+        dict(name="pad_k6_centred", in_c=20, out_c=33, kernel_h=6, kernel_w=6, pad_h=3, pad_w=3, pad_bottom=2,
+             pad_right=2),
+        dict(name="pad_bw_k4", type="binary_weights", in_c=24, kernel_h=4, kernel_w=4, pad_h=2, pad_w=2,
+             pad_bottom=1, pad_right=1, use_beta=True),
+        dict(name="pad_bw_k3_asym_s2", type="binary_weights", in_c=64, out_c=128, stride_h=2, stride_w=2,
+             pad_h=1, pad_w=0, pad_bottom=0, pad_right=2),
+        dict(name="pad_fc_like_trailing", n=3, in_h=4, in_w=5, in_c=40, out_c=20, kernel_h=4, kernel_w=5,
+             pad_h=0, pad_w=0, pad_bottom=1, pad_right=2),
+    ]
+    return [base.with_(**g) for g in geoms]
+
+
+PAD_LAYERS = _pad_layers()
+
+
+@pytest.mark.parametrize("layer", PAD_LAYERS, ids=[l.name for l in PAD_LAYERS])
+def test_asymmetric_padding(dev, layer):
+    """Different leading and trailing padding (the centred window of even
+    kernels), on the specialised, generic and int8 paths."""
+    inputs = workloads.make_inputs(layer, 9000 + PAD_LAYERS.index(layer))
+    _log(f"pad {layer}")
+    ref = oracle.bconv_layer(layer, inputs)
+    assert ref["out"].shape[1:3] == (layer.out_h, layer.out_w)
+    for generic in (False, True):
+        got = parity.run_gpu(layer, inputs, dev, generic=generic)
+        parity.compare(layer, inputs, got, ref=ref)
+    if layer.type != "binary_weights":
+        got = parity.run_gpu(layer, inputs, dev, int8_mfma=True)
+        parity.compare(layer, inputs, got, ref=ref)
+
+
 # ------------------------------------------------ int8 matrix-core comparison path
 
 def _int8_layers():

@@ -37,8 +37,10 @@ MUTANTS = {
     "affine_two_roundings": [("v = fmaf(v, s, b);", "v = (float)(v * s) + b;")],
     "a_map_over_word_width": [("am[p] = sum / (double)in_c;", "am[p] = sum / (double)(words * 32);")],
     "a_map_before_affine": [("sum += fabs(xd[p * in_c + c]);", "sum += fabs((double)x[p * in_c + c]);")],
-    "ceil_mode_output_size": [("return (in + 2 * pad - k) / stride + 1;",
-                               "return (in + 2 * pad - k + stride - 1) / stride + 1;")],
+    "ceil_mode_output_size": [("return (in + pad + pad_end - k) / stride + 1;",
+                               "return (in + pad + pad_end - k + stride - 1) / stride + 1;")],
+    "trailing_pad_is_leading": [("return (in + pad + pad_end - k) / stride + 1;",
+                                 "return (in + 2 * pad - k) / stride + 1;")],
     "epilogue_drops_beta": [("double r = v * scale * bw[((long)i * out_h + oy) * out_w + ox] + bias;",
                              "double r = v * scale + bias;")],
     "relu_clamps_positive": [("if (neuron == ORACLE_NEURON_RELU && r < 0.0) r = 0.0;",
