@@ -81,6 +81,24 @@ __device__ __forceinline__ void store_result(const XArgs &a, long long pix, int 
     __hip_atomic_store(&a.out[o], r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// v of lane i + N of the same 16-lane row (DPP row_shl:N; lanes past the row read 0).
+template <int N>
+__device__ __forceinline__ float row_shl(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0u, __builtin_bit_cast(uint32_t, v), 0x100 + N, 0xf,
+                                                                 0xf, false));
+}
+
+// sum + v[i + K] + ... + v[i + KW - 1] within the 16-lane row, left to right.
+template <int KW, int K = 1>
+__device__ __forceinline__ float add_row_shifted(float sum, float v)
+{
+    if constexpr (K < KW)
+        return add_row_shifted<KW, K + 1>(sum + row_shl<K>(v), v);
+    else
+        return sum;
+}
+
 // Specialised kernel: kernel KHxKW, CW words per pixel, horizontal stride SW,
 // P output pixels per strip.  One wave = one (strip, 64-channel tile).
 template <int KH, int KW, int CW, int SW, int P, bool AND>
@@ -114,13 +132,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void x
     const int oy = (int)(row - imgu * (unsigned)a.out_h);
 
     // beta of pixel `lane` (lanes < P): window sum of the zero-halo A map.
-    // One load brings the strip's KH x NCOL patch (row r in lanes 16r..16r+15);
-    // cross-lane sums then add each window.  Consumed in the epilogue.
+    // Consumed in the epilogue.
     float be_lane = 1.0f;
     if (a.a_pad) {
         const __amdgpu_buffer_rsrc_t ar = make_rsrc(a.a_pad, a.apad_bytes);
         const uint32_t abase = (uint32_t)(((img * a.rows + oy * a.sh) * a.cols + ow0 * SW) * 4);
-        if constexpr (KH <= 4 && NCOL <= 16) {
+        if constexpr (SW == 1 && NCOL <= 16) {
+            // Lane c < NCOL sums column c of the strip's KH x NCOL patch; pixel
+            // `lane` then adds columns lane .. lane + KW - 1 with DPP row_shl
+            // (lane i reads lane i + kx of its 16-lane row).  Past the last
+            // column of a ragged strip the patch reads zero (buffer range) or a
+            // neighbouring pixel's value, which feed only pixels not stored.
+            const uint32_t coff = lane < NCOL ? (uint32_t)(lane * 4) : 0x80000000u;
+            float colsum = 0.0f;
+#pragma unroll
+            for (int r = 0; r < KH; ++r)
+                colsum += __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ar, coff, abase + r * a.cols * 4, 0));
+            be_lane = add_row_shifted<KW>(colsum, colsum) * (1.0f / (float)(KH * KW));
+        } else if constexpr (KH <= 4 && NCOL <= 16) {
+            // One load brings the strip's KH x NCOL patch (row r in lanes
+            // 16r..16r+15); cross-lane sums then add each window.
             const int pr = lane >> 4, pc = lane & 15;
             // the patch stays inside the zero-halo map except past the last
             // column of a ragged strip: those read zero (buffer range) or a
@@ -245,39 +276,61 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void x
     const uint32_t obase =
         __builtin_amdgcn_readfirstlane((uint32_t)(((img * a.out_h + oy) * a.out_w + ow0) * a.out_c) * 4u);
     const uint32_t ostep = (uint32_t)a.out_c * 4u;
+    // the output value's integer part: window sum (XNOR with its border correction)
+    auto window_value = [&](int p, int ox) -> int {
+        if (AND) return (int)acc[p];  // a zero word at a padded tap adds nothing
+        const int ix0 = ox * SW - a.pw;
+        const int c0 = ix0 < 0 ? -ix0 : 0;
+        const int c1 = a.in_w - ix0 < KW ? a.in_w - ix0 : KW;
+        const int valid = (r1 - r0) * (c1 - c0);
+        int corr = 0;
+        if (valid != KH * KW) {
+            // set weight bits at padded taps = total - in-image rectangle
+            // (c0, c1 are wave-uniform: a select chain, no register indexing)
+            int a0 = 0, a1 = 0, b0 = 0, b1 = 0;
 #pragma unroll
-    for (int p = 0; p < P; ++p) {
-        const int ox = ow0 + p;
-        if (ox >= a.out_w) break;
-        int v;
-        if (AND) {
-            v = (int)acc[p];  // a zero word at a padded tap adds nothing
-        } else {
-            const int ix0 = ox * SW - a.pw;
-            const int c0 = ix0 < 0 ? -ix0 : 0;
-            const int c1 = a.in_w - ix0 < KW ? a.in_w - ix0 : KW;
-            const int valid = (r1 - r0) * (c1 - c0);
-            int corr = 0;
-            if (valid != KH * KW) {
-                // set weight bits at padded taps = total - in-image rectangle
-                // (c0, c1 are wave-uniform: a select chain, no register indexing)
-                int a0 = 0, a1 = 0, b0 = 0, b1 = 0;
-#pragma unroll
-                for (int c = 0; c <= KW; ++c) {
-                    if (c == c0) { a0 = rt0[c]; a1 = rt1[c]; }
-                    if (c == c1) { b0 = rt0[c]; b1 = rt1[c]; }
-                }
-                corr = rtotal - (b1 - b0 - a1 + a0);
+            for (int c = 0; c <= KW; ++c) {
+                if (c == c0) { a0 = rt0[c]; a1 = rt1[c]; }
+                if (c == c1) { b0 = rt0[c]; b1 = rt1[c]; }
             }
-            v = a.in_c * valid - 2 * ((int)acc[p] - corr);
+            corr = rtotal - (b1 - b0 - a1 + a0);
         }
-        const float be = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(be_lane), p));
-        if (a.bits_out)
+        return a.in_c * valid - 2 * ((int)acc[p] - corr);
+    };
+    if (a.bits_out) {
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            const int ox = ow0 + p;
+            if (ox >= a.out_w) break;
+            const float be = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(be_lane), p));
             store_tile_bits(a.bits_out, ((long long)img * a.out_h + oy) * a.out_w + ox, a.out_words, (int)tile,
-                            co_ok && sign_bit(epilogue_value((float)v, sc, be, bi, a.relu)));
-        else
-            store_result_buf(a, orr, obase + (uint32_t)p * ostep, co, v, sc, bi, be);
+                            co_ok && sign_bit(epilogue_value((float)window_value(p, ox), sc, be, bi, a.relu)));
+        }
+        return;
     }
+    // One unrolled loop per output form (window sums, values with and without
+    // ReLU), so no per-pixel select between them.  Lanes past out_c store at an
+    // out-of-range offset, which the buffer range check discards.
+    const uint32_t coff = co_ok ? (uint32_t)(co * 4) : 0x80000000u;
+    auto store_all = [&](auto value_bits) {
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            const int ox = ow0 + p;
+            if (ox >= a.out_w) break;
+            const float be = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(be_lane), p));
+            __builtin_amdgcn_raw_buffer_store_b32(value_bits(window_value(p, ox), be), orr, coff,
+                                                  __builtin_amdgcn_readfirstlane(obase + (uint32_t)p * ostep), kStoreSc1);
+        }
+    };
+    if (a.acc_out)
+        store_all([](int v, float) { return (uint32_t)v; });
+    else if (a.relu)
+        store_all([&](int v, float be) {
+            const float r = __builtin_fmaf((float)v * sc, be, bi);
+            return __builtin_bit_cast(uint32_t, (r < 0.0f) ? 0.0f : r);
+        });
+    else
+        store_all([&](int v, float be) { return __builtin_bit_cast(uint32_t, __builtin_fmaf((float)v * sc, be, bi)); });
 }
 
 // Any geometry: one wave = one output pixel and a 64-channel tile; taps
