@@ -24,7 +24,10 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 TYPE_CODES = {"binary_weights": 0, "xnor": 1, "and": 2}
-NEURON_CODES = {"none": 0, "relu": 1}
+NEURON_CODES = {"none": 0, "relu": 1,
+                "leaky_relu": 2, "linear": 3, "sigmoid": 4,
+                "hard_sigmoid": 5, "tanh": 6, "absolute": 7, "softplus": 8,
+                "softsign": 9, "elu": 10, "clamp": 11}
 
 _lib = None
 
@@ -49,7 +52,7 @@ def load(path: Optional[str] = None):
     lib = ctypes.CDLL(p)
     i, f, vp = ctypes.c_int, ctypes.c_float, ctypes.c_void_p
     lib.oracle_bconv.restype = i
-    lib.oracle_bconv.argtypes = [i] * 16 + [f] + [vp] * 12 + [i]
+    lib.oracle_bconv.argtypes = [i] * 16 + [f, f, f] + [vp] * 12 + [i]
     lib.oracle_out_dim.restype = i
     lib.oracle_out_dim.argtypes = [i, i, i, i]
     lib.oracle_out_dim2.restype = i
@@ -71,7 +74,8 @@ def out_dim(size: int, kernel: int, stride: int, pad: int, pad_end: Optional[int
 def bconv(x: np.ndarray, weight_bits: np.ndarray, *, type: str, out_c: int,
           kernel=(1, 1), stride=(1, 1), pad=(0, 0), pad_end=None, output_scale=None, output_bias=None,
           input_scale=None, input_bias=None, use_beta: bool = False, neuron: str = "none",
-          scale_value: float = 1.0, threads: int = 0, want=("out", "acc", "beta", "a_map", "signs"),
+          scale_value: float = 1.0, neuron_a: float = 0.0, neuron_b: float = 0.0, threads: int = 0,
+          want=("out", "acc", "beta", "a_map", "signs"),
           lib=None) -> dict:
     """Evaluate binary convolution on the CPU.
 
@@ -111,7 +115,8 @@ def bconv(x: np.ndarray, weight_bits: np.ndarray, *, type: str, out_c: int,
     a_map = np.empty((n, h, w), np.float64) if ("a_map" in want and use_beta) else None
     beta = np.empty((n, oh, ow), np.float64) if "beta" in want else None
     rc = lib.oracle_bconv(n, h, w, c, out_c, kh, kw, sh, sw, ph, pw, phe, pwe, t, int(bool(use_beta)),
-                          NEURON_CODES[neuron], float(scale_value), _ptr(x), _ptr(weight_bits),
+                          NEURON_CODES[neuron], float(scale_value), float(neuron_a), float(neuron_b),
+                          _ptr(x), _ptr(weight_bits),
                           _ptr(output_scale), _ptr(output_bias), _ptr(input_scale),
                           _ptr(input_bias), _ptr(out), _ptr(acc_i), _ptr(acc_r), _ptr(signs),
                           _ptr(a_map), _ptr(beta), int(threads))
@@ -129,4 +134,5 @@ def bconv_layer(layer, inputs: dict, threads: int = 0, lib=None, **kw) -> dict:
                  output_scale=inputs.get("output_scale"),
                  output_bias=inputs.get("output_bias"), input_scale=inputs.get("input_scale"),
                  input_bias=inputs.get("input_bias"), use_beta=layer.use_beta,
-                 neuron=layer.neuron, scale_value=layer.scale_value, threads=threads, lib=lib, **kw)
+                 neuron=layer.neuron, scale_value=layer.scale_value, neuron_a=layer.neuron_a,
+                 neuron_b=layer.neuron_b, threads=threads, lib=lib, **kw)

@@ -43,8 +43,52 @@
 #define ORACLE_XNOR 1
 #define ORACLE_AND 2
 
+/* Activation applied last (MPSCNNBinaryConvolution, Overview, closing
+ * sentence: "the normal activation neuron").  The page names no set; these
+ * are the usual element-wise activations, with parameters a and b. */
 #define ORACLE_NEURON_NONE 0
 #define ORACLE_NEURON_RELU 1
+#define ORACLE_NEURON_LEAKY_RELU 2
+#define ORACLE_NEURON_LINEAR 3
+#define ORACLE_NEURON_SIGMOID 4
+#define ORACLE_NEURON_HARD_SIGMOID 5
+#define ORACLE_NEURON_TANH 6
+#define ORACLE_NEURON_ABSOLUTE 7
+#define ORACLE_NEURON_SOFTPLUS 8
+#define ORACLE_NEURON_SOFTSIGN 9
+#define ORACLE_NEURON_ELU 10
+#define ORACLE_NEURON_CLAMP 11
+#define ORACLE_NEURON_COUNT 12
+
+/* Each activation from its definition, in double:
+ *   relu        r < 0 ? 0 : r              leaky_relu  r < 0 ? a*r : r
+ *   linear      a*r + b                    sigmoid     1 / (1 + e^-r)
+ *   hard_sigmoid min(max(a*r + b, 0), 1)   tanh        a * tanh(b*r)
+ *   absolute    |r|                        softplus    a * log(1 + e^(b*r))
+ *   softsign    r / (1 + |r|)              elu         r < 0 ? a*(e^r - 1) : r
+ *   clamp       min(max(r, a), b)
+ * softplus is evaluated as max(z, 0) + log1p(e^-|z|), the same function
+ * without overflow of e^z. */
+static double neuron_value(int neuron, double a, double b, double r)
+{
+    switch (neuron) {
+    case ORACLE_NEURON_RELU: return r < 0.0 ? 0.0 : r;
+    case ORACLE_NEURON_LEAKY_RELU: return r < 0.0 ? a * r : r;
+    case ORACLE_NEURON_LINEAR: return a * r + b;
+    case ORACLE_NEURON_SIGMOID: return 1.0 / (1.0 + exp(-r));
+    case ORACLE_NEURON_HARD_SIGMOID: return fmin(fmax(a * r + b, 0.0), 1.0);
+    case ORACLE_NEURON_TANH: return a * tanh(b * r);
+    case ORACLE_NEURON_ABSOLUTE: return fabs(r);
+    case ORACLE_NEURON_SOFTPLUS: {
+        const double z = b * r;
+        return a * (fmax(z, 0.0) + log1p(exp(-fabs(z))));
+    }
+    case ORACLE_NEURON_SOFTSIGN: return r / (1.0 + fabs(r));
+    case ORACLE_NEURON_ELU: return r < 0.0 ? a * expm1(r) : r;
+    case ORACLE_NEURON_CLAMP: return fmin(fmax(r, a), b);
+    default: return r;
+    }
+}
 
 int oracle_out_dim2(int in, int k, int stride, int pad, int pad_end)
 {
@@ -120,7 +164,8 @@ static int input_sign(float v, int type)
 int oracle_bconv(int n, int in_h, int in_w, int in_c, int out_c, int kernel_h, int kernel_w,
                  int stride_h, int stride_w, int pad_h, int pad_w, int pad_h_end, int pad_w_end,
                  int type, int use_beta,
-                 int neuron, float scale_value, const float *x, const uint32_t *weight_bits,
+                 int neuron, float scale_value, float neuron_a, float neuron_b, const float *x,
+                 const uint32_t *weight_bits,
                  const float *output_scale, const float *output_bias, const float *input_scale,
                  const float *input_bias, double *out, int32_t *acc_int, double *acc_real,
                  int8_t *signs, double *a_map, double *beta, int n_threads)
@@ -130,7 +175,7 @@ int oracle_bconv(int n, int in_h, int in_w, int in_c, int out_c, int kernel_h, i
         pad_w_end < 0)
         return -1;
     if (type != ORACLE_BINARY_WEIGHTS && type != ORACLE_XNOR && type != ORACLE_AND) return -1;
-    if (neuron != ORACLE_NEURON_NONE && neuron != ORACLE_NEURON_RELU) return -1;
+    if (neuron < 0 || neuron >= ORACLE_NEURON_COUNT) return -1;
     if (!x || !weight_bits || !out) return -1;
 
     const int out_h = oracle_out_dim2(in_h, kernel_h, stride_h, pad_h, pad_h_end);
@@ -237,9 +282,8 @@ int oracle_bconv(int n, int in_h, int in_w, int in_c, int out_c, int kernel_h, i
                     if (acc_real) acc_real[oo] = accd;
                     double scale = output_scale ? (double)output_scale[co] : (double)scale_value;
                     double bias = output_bias ? (double)output_bias[co] : 0.0;
-                    double r = v * scale * bw[((long)i * out_h + oy) * out_w + ox] + bias;
-                    if (neuron == ORACLE_NEURON_RELU && r < 0.0) r = 0.0;
-                    out[oo] = r;
+                    const double r = v * scale * bw[((long)i * out_h + oy) * out_w + ox] + bias;
+                    out[oo] = neuron_value(neuron, (double)neuron_a, (double)neuron_b, r);
                 }
             }
         }

@@ -28,7 +28,8 @@ import numpy as np
 import torch
 
 TYPES = ("binary_weights", "xnor", "and")
-NEURONS = ("none", "relu")
+NEURONS = ("none", "relu", "leaky_relu", "linear", "sigmoid", "hard_sigmoid", "tanh", "absolute", "softplus",
+           "softsign", "elu", "clamp")
 
 
 @dataclasses.dataclass(frozen=True)
@@ -57,6 +58,9 @@ class Layer:
     # trailing (bottom / right) zero padding; None = the leading one
     pad_bottom: Optional[int] = None
     pad_right: Optional[int] = None
+    # activation parameters (see the neuron list of the C header)
+    neuron_a: float = 0.0
+    neuron_b: float = 0.0
 
     @property
     def pad_h_end(self) -> int:

@@ -369,6 +369,65 @@ def check_epilogue_closed_form(lib):
     np.testing.assert_allclose(rb["out"][0], acc * sc * absx[:, :, None] + bi, rtol=1e-15)
 
 
+# ------------------------------------------------------------------ neurons
+
+_NEURON_RS = np.array([-6.0, -2.5, -1.0, -0.5, -0.25, 0.0, 0.25, 0.5, 1.0, 2.5, 6.0])
+
+
+def _neuron_outputs(lib, neuron, a=0.0, b=0.0, rs=_NEURON_RS):
+    """Outputs of a 1x1 XNOR layer with Cin = 1 whose pre-activation values are
+    exactly `rs`: input +1, weight bits 1 (acc = +1), scale 1, bias r - 1."""
+    o = len(rs)
+    bias = (rs - 1.0).astype(np.float32)
+    assert np.array_equal(bias.astype(np.float64) + 1.0, rs)
+    r = _run(lib, np.ones((1, 1, 1, 1), np.float32), np.ones((o, 1, 1, 1), np.uint32), "xnor", o,
+             output_scale=np.ones(o, np.float32), output_bias=bias, neuron=neuron, neuron_a=a, neuron_b=b)
+    return r["out"][0, 0, 0]
+
+
+def check_neuron_closed_forms(lib):
+    """Piecewise-linear and rational activations on exactly representable
+    pre-activation values, against hand-computed results."""
+    rs = _NEURON_RS
+    np.testing.assert_array_equal(_neuron_outputs(lib, "none"), rs)
+    np.testing.assert_array_equal(_neuron_outputs(lib, "relu"), [0, 0, 0, 0, 0, 0, 0.25, 0.5, 1, 2.5, 6])
+    np.testing.assert_array_equal(_neuron_outputs(lib, "leaky_relu", a=0.125),
+                                  [-0.75, -0.3125, -0.125, -0.0625, -0.03125, 0, 0.25, 0.5, 1, 2.5, 6])
+    np.testing.assert_array_equal(_neuron_outputs(lib, "linear", a=2.0, b=-0.5),
+                                  [-12.5, -5.5, -2.5, -1.5, -1, -0.5, 0, 0.5, 1.5, 4.5, 11.5])
+    np.testing.assert_array_equal(_neuron_outputs(lib, "absolute"), [6, 2.5, 1, 0.5, 0.25, 0, 0.25, 0.5, 1, 2.5, 6])
+    np.testing.assert_array_equal(_neuron_outputs(lib, "hard_sigmoid", a=0.25, b=0.5),
+                                  [0, 0, 0.25, 0.375, 0.4375, 0.5, 0.5625, 0.625, 0.75, 1, 1])
+    np.testing.assert_array_equal(_neuron_outputs(lib, "clamp", a=-1.0, b=2.0),
+                                  [-1, -1, -1, -0.5, -0.25, 0, 0.25, 0.5, 1, 2, 2])
+    np.testing.assert_allclose(_neuron_outputs(lib, "softsign"),
+                               [-6 / 7, -5 / 7, -1 / 2, -1 / 3, -1 / 5, 0, 1 / 5, 1 / 3, 1 / 2, 5 / 7, 6 / 7],
+                               rtol=1e-15, atol=0)
+
+
+def check_neuron_identities(lib):
+    """The exponential activations through identities that need no math
+    library: sigmoid(0) = 1/2 and sigmoid(r) + sigmoid(-r) = 1; a*tanh(b*r) =
+    a*(2*sigmoid(2*b*r) - 1); softplus(0) = a*ln 2 and
+    softplus(r) - softplus(-r) = a*b*r; elu(r) = a*(e^r - 1) for r < 0 with
+    e^r = sigmoid(r) / (1 - sigmoid(r))."""
+    rs = _NEURON_RS
+    s = _neuron_outputs(lib, "sigmoid")
+    assert s[rs == 0][0] == 0.5
+    np.testing.assert_allclose(s + s[::-1], 1.0, rtol=0, atol=1e-15)
+    assert np.all(np.diff(s) > 0) and np.all((s > 0) & (s < 1))
+    t = _neuron_outputs(lib, "tanh", a=2.0, b=0.5)   # 2*b*r = r
+    np.testing.assert_allclose(t, 2.0 * (2.0 * s - 1.0), rtol=0, atol=1e-14)
+    sp = _neuron_outputs(lib, "softplus", a=1.5, b=2.0)
+    np.testing.assert_allclose(sp[rs == 0][0], 1.5 * 0.6931471805599453, rtol=1e-15)
+    np.testing.assert_allclose(sp - sp[::-1], 3.0 * rs, rtol=0, atol=1e-13)
+    assert np.all(sp > 0)
+    e = _neuron_outputs(lib, "elu", a=0.5)
+    neg = rs < 0
+    np.testing.assert_array_equal(e[~neg], rs[~neg])
+    np.testing.assert_allclose(e[neg], 0.5 * (s[neg] / (1.0 - s[neg]) - 1.0), rtol=1e-13, atol=0)
+
+
 # -------------------------------------------------------------- sign / affine
 
 def _fma_f32(x, s, b) -> np.float32:
@@ -477,5 +536,5 @@ ALL_CHECKS = [
     check_binary_weights_conv, check_all_ones_closed_form, check_beta_constant_input,
     check_a_map_definition, check_epilogue_closed_form, check_sign_under_affine,
     check_tail_bits_ignored, check_degenerate_single_channel,
-    check_accumulator_parity_and_range,
+    check_accumulator_parity_and_range, check_neuron_closed_forms, check_neuron_identities,
 ]

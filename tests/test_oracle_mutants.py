@@ -43,8 +43,17 @@ MUTANTS = {
                                  "return (in + 2 * pad - k) / stride + 1;")],
     "epilogue_drops_beta": [("double r = v * scale * bw[((long)i * out_h + oy) * out_w + ox] + bias;",
                              "double r = v * scale + bias;")],
-    "relu_clamps_positive": [("if (neuron == ORACLE_NEURON_RELU && r < 0.0) r = 0.0;",
-                              "if (neuron == ORACLE_NEURON_RELU && r > 0.0) r = 0.0;")],
+    "relu_clamps_positive": [("case ORACLE_NEURON_RELU: return r < 0.0 ? 0.0 : r;",
+                              "case ORACLE_NEURON_RELU: return r > 0.0 ? 0.0 : r;")],
+    "sigmoid_sign": [("return 1.0 / (1.0 + exp(-r));", "return 1.0 / (1.0 + exp(r));")],
+    "tanh_drops_scale": [("return a * tanh(b * r);", "return tanh(b * r);")],
+    "softplus_drops_max": [("return a * (fmax(z, 0.0) + log1p(exp(-fabs(z))));",
+                            "return a * log1p(exp(-fabs(z)));")],
+    "elu_scales_positive": [("return r < 0.0 ? a * expm1(r) : r;", "return r < 0.0 ? a * expm1(r) : a * r;")],
+    "clamp_bounds_swapped": [("return fmin(fmax(r, a), b);", "return fmin(fmax(r, b), a);")],
+    "leaky_slope_on_positive": [("return r < 0.0 ? a * r : r;", "return r < 0.0 ? r : a * r;")],
+    "hard_sigmoid_no_upper_clamp": [("return fmin(fmax(a * r + b, 0.0), 1.0);", "return fmax(a * r + b, 0.0);")],
+    "softsign_drops_abs": [("return r / (1.0 + fabs(r));", "return r / (1.0 + r);")],
     "missing_bias_is_one": [("(double)output_bias[co] : 0.0;", "(double)output_bias[co] : 1.0;")],
     "scale_value_ignored": [("(double)output_scale[co] : (double)scale_value;",
                              "(double)output_scale[co] : 1.0;")],
