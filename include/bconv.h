@@ -42,7 +42,7 @@
  *     BCONV_FLAG_USE_BETA_SCALING.  It applies to all three forms.
  *   - A missing output scale array means the scalar desc.scale_value; missing
  *     biases mean 0; a missing input scale means 1.
- *   - neuron: none, or ReLU  r < 0 ? 0 : r.
+ *   - neuron: one of bconv_neuron_t, applied last; ReLU is r < 0 ? 0 : r.
  *
  * Results: XNOR/AND window sums are exact integers; the fp32 epilogue and
  * the binaryWeights fp32 accumulation agree with an exact evaluation to a
@@ -97,11 +97,25 @@ enum {
 };
 
 /* The activation applied last (MPSCNNBinaryConvolution, Overview, closing
- * sentence of the description). */
+ * sentence of the description: "the normal activation neuron"; the page
+ * names no set).  r is the value scale*beta*sum + bias; a and b are
+ * desc.neuron_a / desc.neuron_b.  Each is evaluated in fp32 (exp, tanh,
+ * log1p and expm1 of the device math library). */
 typedef enum {
-    BCONV_NEURON_NONE = 0,
-    BCONV_NEURON_RELU = 1
+    BCONV_NEURON_NONE = 0,          /* r */
+    BCONV_NEURON_RELU = 1,          /* r < 0 ? 0 : r (NaN passes) */
+    BCONV_NEURON_LEAKY_RELU = 2,    /* r < 0 ? a*r : r */
+    BCONV_NEURON_LINEAR = 3,        /* a*r + b */
+    BCONV_NEURON_SIGMOID = 4,       /* 1 / (1 + e^-r) */
+    BCONV_NEURON_HARD_SIGMOID = 5,  /* min(max(a*r + b, 0), 1) */
+    BCONV_NEURON_TANH = 6,          /* a * tanh(b*r) */
+    BCONV_NEURON_ABSOLUTE = 7,      /* |r| */
+    BCONV_NEURON_SOFTPLUS = 8,      /* a * log(1 + e^(b*r)), as max(z,0) + log1p(e^-|z|), z = b*r */
+    BCONV_NEURON_SOFTSIGN = 9,      /* r / (1 + |r|) */
+    BCONV_NEURON_ELU = 10,          /* r < 0 ? a*(e^r - 1) : r */
+    BCONV_NEURON_CLAMP = 11         /* min(max(r, a), b) */
 } bconv_neuron_t;
+#define BCONV_NEURON_COUNT 12
 
 /* Layer shape (the convolution descriptor of the pages: kernel width/height,
  * strides, groups).  The batch size is given per call. */
@@ -117,6 +131,7 @@ typedef struct {
     int32_t pad_h_end, pad_w_end; /* trailing (bottom, right) zero padding,
                                      0 <= pad_end < kernel; equal to pad_h / pad_w
                                      for the usual symmetric padding */
+    float neuron_a, neuron_b;  /* activation parameters a, b (see bconv_neuron_t) */
 } bconv_desc_t;
 
 /* Where the per-step intermediates sit in a forward call's workspace, for

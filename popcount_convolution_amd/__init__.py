@@ -38,10 +38,12 @@ class BinaryConvolution:
                  stride: tuple = (1, 1), pad: tuple = (0, 0), pad_end=None, type: str = "xnor",
                  weight_bits: np.ndarray, output_scale=None, output_bias=None,
                  input_scale=None, input_bias=None, use_beta: bool = False,
-                 neuron: str = "none", scale_value: float = 1.0, int8_mfma: bool = False):
+                 neuron: str = "none", scale_value: float = 1.0, int8_mfma: bool = False,
+                 neuron_a: float = 0.0, neuron_b: float = 0.0):
         pe = pad if pad_end is None else pad_end
         self.desc = make_desc(in_h, in_w, in_c, out_c, kernel[0], kernel[1], stride[0], stride[1],
-                              pad[0], pad[1], 1, NEURON_CODES[neuron], scale_value, pe[0], pe[1])
+                              pad[0], pad[1], 1, NEURON_CODES[neuron], scale_value, pe[0], pe[1],
+                              neuron_a, neuron_b)
         self.type = TYPE_CODES[type]
         self.flags = (BCONV_FLAG_USE_BETA_SCALING if use_beta else BCONV_FLAG_NONE) | \
             (BCONV_FLAG_INT8_MFMA if int8_mfma else BCONV_FLAG_NONE)
@@ -60,7 +62,8 @@ class BinaryConvolution:
                    weight_bits=inputs["weight_bits"], output_scale=inputs.get("output_scale"),
                    output_bias=inputs.get("output_bias"), input_scale=inputs.get("input_scale"),
                    input_bias=inputs.get("input_bias"), use_beta=layer.use_beta,
-                   neuron=layer.neuron, scale_value=layer.scale_value, int8_mfma=int8_mfma)
+                   neuron=layer.neuron, scale_value=layer.scale_value, int8_mfma=int8_mfma,
+                   neuron_a=layer.neuron_a, neuron_b=layer.neuron_b)
 
     def workspace_bytes(self, n: int) -> int:
         return bconv_workspace_size(self.handle, n)

@@ -35,9 +35,11 @@ BCONV_FLAG_INT8_MFMA = 2
 # bconv_neuron_t
 BCONV_NEURON_NONE = 0
 BCONV_NEURON_RELU = 1
+NEURON_NAMES = ("none", "relu", "leaky_relu", "linear", "sigmoid", "hard_sigmoid", "tanh", "absolute", "softplus",
+                "softsign", "elu", "clamp")
 
 TYPE_CODES = {"binary_weights": BCONV_BINARY_WEIGHTS, "xnor": BCONV_XNOR, "and": BCONV_AND}
-NEURON_CODES = {"none": BCONV_NEURON_NONE, "relu": BCONV_NEURON_RELU}
+NEURON_CODES = {name: code for code, name in enumerate(NEURON_NAMES)}
 SIZE_MAX = ctypes.c_size_t(-1).value
 
 
@@ -55,7 +57,8 @@ class bconv_desc_t(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "in_h", "in_w", "in_c", "out_c", "kernel_h", "kernel_w", "stride_h", "stride_w",
         "pad_h", "pad_w", "groups", "neuron")] + [("scale_value", ctypes.c_float)] + \
-        [("pad_h_end", ctypes.c_int32), ("pad_w_end", ctypes.c_int32)]
+        [("pad_h_end", ctypes.c_int32), ("pad_w_end", ctypes.c_int32),
+         ("neuron_a", ctypes.c_float), ("neuron_b", ctypes.c_float)]
 
 
 class bconv_workspace_layout_t(ctypes.Structure):
@@ -141,11 +144,11 @@ def _ptr(x) -> Optional[int]:
 
 def make_desc(in_h, in_w, in_c, out_c, kernel_h, kernel_w, stride_h=1, stride_w=1, pad_h=0,
               pad_w=0, groups=1, neuron=BCONV_NEURON_NONE, scale_value=1.0, pad_h_end=None,
-              pad_w_end=None) -> bconv_desc_t:
+              pad_w_end=None, neuron_a=0.0, neuron_b=0.0) -> bconv_desc_t:
     """Trailing padding defaults to the leading one (symmetric padding)."""
     return bconv_desc_t(in_h, in_w, in_c, out_c, kernel_h, kernel_w, stride_h, stride_w, pad_h,
                         pad_w, groups, neuron, scale_value, pad_h if pad_h_end is None else pad_h_end,
-                        pad_w if pad_w_end is None else pad_w_end)
+                        pad_w if pad_w_end is None else pad_w_end, neuron_a, neuron_b)
 
 
 def bconv_validate_desc(desc: bconv_desc_t, type: int, flags: int) -> int:

@@ -74,7 +74,7 @@ bconv_status_t check_desc(const bconv_desc_t *d, int32_t type, uint32_t flags)
         return fail(BCONV_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", flags);
     if ((flags & BCONV_FLAG_INT8_MFMA) && type == BCONV_BINARY_WEIGHTS)
         return fail(BCONV_ERR_INVALID_ARGUMENT, "BCONV_FLAG_INT8_MFMA applies to XNOR and AND only");
-    if (d->neuron != BCONV_NEURON_NONE && d->neuron != BCONV_NEURON_RELU)
+    if (d->neuron < 0 || d->neuron >= BCONV_NEURON_COUNT)
         return fail(BCONV_ERR_INVALID_ARGUMENT, "unknown neuron %d", d->neuron);
     if (d->groups <= 0) return fail(BCONV_ERR_INVALID_ARGUMENT, "groups must be >= 1");
     if (d->groups != 1) return fail(BCONV_ERR_UNSUPPORTED, "groups > 1 is not supported");
@@ -266,7 +266,7 @@ bconv_status_t forward_impl(bconv_t h, void *stream, int32_t n, const float *in,
     ep.scale_value = d.scale_value;
     ep.a_pad = a_map;
     ep.beta_out = beta;
-    ep.relu = d.neuron == BCONV_NEURON_RELU;
+    ep.neuron = bconv::Neuron{d.neuron, d.neuron_a, d.neuron_b};
     if (sink == Sink::Bits) {
         ep.bits_out = static_cast<uint32_t *>(dst);
         ep.out_words = out_words;

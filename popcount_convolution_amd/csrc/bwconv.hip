@@ -25,7 +25,7 @@ struct BwArgs {
     float *beta_out;
     int rows, cols;
     float scale_value;
-    int relu;
+    Neuron neuron;
     float *out;
     float *acc_out;
     uint32_t *bits_out;  // packed sign bits instead of out (see Epilogue)
@@ -115,7 +115,7 @@ __global__ __launch_bounds__(256) void bwconv_kernel(BwArgs a)
             if (co >= a.out_c) break;
             const float sc = a.scale ? a.scale[co] : a.scale_value;
             const float bi = a.bias ? a.bias[co] : 0.0f;
-            if (sign_bit(epilogue_value(acc[q], sc, be, bi, a.relu))) word |= 1u << q;
+            if (sign_bit(epilogue_value(acc[q], sc, be, bi, a.neuron))) word |= 1u << q;
         }
         store_through(&a.bits_out[m * a.out_words + cb], word);
         return;
@@ -131,9 +131,8 @@ __global__ __launch_bounds__(256) void bwconv_kernel(BwArgs a)
         }
         const float sc = a.scale ? a.scale[co] : a.scale_value;
         const float bi = a.bias ? a.bias[co] : 0.0f;
-        float r = __builtin_fmaf(acc[q] * sc, be, bi);
-        if (a.relu) r = (r < 0.0f) ? 0.0f : r;
-        __hip_atomic_store(&a.out[o], r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&a.out[o], epilogue_value(acc[q], sc, be, bi, a.neuron), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -165,7 +164,7 @@ hipError_t launch_bwconv(const Geom &g, const Launch &L, const float *x, const f
     a.rows = g.bits_rows;
     a.cols = g.bits_cols;
     a.scale_value = e.scale_value;
-    a.relu = e.relu;
+    a.neuron = e.neuron;
     a.out = out;
     a.acc_out = acc_out;
     a.bits_out = e.bits_out;

@@ -72,7 +72,7 @@ struct MmaArgs {
     const float *a_pad;  // zero-halo A map or nullptr (beta = 1)
     float *beta_out;
     float scale_value;
-    int relu;
+    Neuron neuron;
     float *out;
     float *acc_out;
     uint32_t *bits_out;  // packed sign bits instead of out (see Epilogue)
@@ -355,7 +355,7 @@ __global__ __launch_bounds__(kThreads) void bwmma_kernel(MmaArgs a)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int co = ntile * kChanTile + 16 * (keep + u) + 4 * (lane >> 4) + r;
-                const float y = epilogue_value(res[u][r], sc[u][r], be, bi[u][r], a.relu);
+                const float y = epilogue_value(res[u][r], sc[u][r], be, bi[u][r], a.neuron);
                 if (co < a.out_c && sign_bit(y)) part |= 1u << (16 * u + 4 * (lane >> 4) + r);
             }
         part |= __shfl_xor(part, 16);
@@ -372,11 +372,7 @@ __global__ __launch_bounds__(kThreads) void bwmma_kernel(MmaArgs a)
         f32x4 v = res[u];
         if (!a.acc_out) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float o = __builtin_fmaf(v[r] * sc[u][r], be, bi[u][r]);
-                if (a.relu) o = (o < 0.0f) ? 0.0f : o;
-                v[r] = o;
-            }
+            for (int r = 0; r < 4; ++r) v[r] = epilogue_value(v[r], sc[u][r], be, bi[u][r], a.neuron);
         }
         const uint32_t off = (uint32_t)(pix * a.out_c + co) * 4u;
         if (a.vec_out && co + 3 < a.out_c) {
@@ -464,7 +460,7 @@ hipError_t launch_bwmma(const Geom &g, const Launch &L, const float *x, const fl
     a.a_pad = e.a_pad;
     a.beta_out = e.beta_out;
     a.scale_value = e.scale_value;
-    a.relu = e.relu;
+    a.neuron = e.neuron;
     a.out = out;
     a.acc_out = acc_out;
     a.bits_out = e.bits_out;

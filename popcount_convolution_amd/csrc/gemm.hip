@@ -36,7 +36,7 @@ struct GArgs {
     const float *a_pad;     // A map [n][H*W] or nullptr (beta = 1)
     float *beta_out;        // [n]
     float scale_value;
-    int relu;
+    Neuron neuron;
     float *out;
     int32_t *acc_out;
     uint32_t *bits_out;     // packed sign bits instead of out (see Epilogue)
@@ -148,7 +148,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void b
             continue;
         }
         const float be = a.a_pad ? rbeta[r] : 1.0f;
-        const float res = epilogue_value((float)v, sc, be, bi, a.relu);
+        const float res = epilogue_value((float)v, sc, be, bi, a.neuron);
         if (a.bits_out) {
             store_tile_bits(a.bits_out, m0 + r, a.out_words, (int)tile, co_ok && sign_bit(res));
             continue;
@@ -221,7 +221,7 @@ hipError_t launch_gemm(const Geom &g, const Launch &L, int and_mode, const uint3
     a.a_pad = e.a_pad;
     a.beta_out = e.beta_out;
     a.scale_value = e.scale_value;
-    a.relu = e.relu;
+    a.neuron = e.neuron;
     a.out = out;
     a.acc_out = acc_out;
     a.bits_out = e.bits_out;

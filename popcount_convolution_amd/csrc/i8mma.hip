@@ -159,7 +159,7 @@ struct I8Args {
     const float *a_pad;
     float *beta_out;
     float scale_value;
-    int relu;
+    Neuron neuron;
     float *out;
     int32_t *acc_out;
     uint32_t *bits_out;  // packed sign bits instead of out (see Epilogue)
@@ -293,7 +293,7 @@ __global__ __launch_bounds__(kThreads) void i8mma_kernel(I8Args a)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int co = ntile * kChanTile + 16 * (keep + u) + 4 * (lane >> 4) + r;
-                const float y = epilogue_value((float)res[u][r], sc[u][r], be, bi[u][r], a.relu);
+                const float y = epilogue_value((float)res[u][r], sc[u][r], be, bi[u][r], a.neuron);
                 if (co < a.out_c && sign_bit(y)) part |= 1u << (16 * u + 4 * (lane >> 4) + r);
             }
         part |= __shfl_xor(part, 16);
@@ -313,11 +313,7 @@ __global__ __launch_bounds__(kThreads) void i8mma_kernel(I8Args a)
         } else {
             f32x4 v;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float o = __builtin_fmaf((float)res[u][r] * sc[u][r], be, bi[u][r]);
-                if (a.relu) o = (o < 0.0f) ? 0.0f : o;
-                v[r] = o;
-            }
+            for (int r = 0; r < 4; ++r) v[r] = epilogue_value((float)res[u][r], sc[u][r], be, bi[u][r], a.neuron);
             w = __builtin_bit_cast(u32x4, v);
         }
         const uint32_t off = (uint32_t)(pix * a.out_c + co) * 4u;
@@ -410,7 +406,7 @@ hipError_t launch_i8mma(const Geom &g, const Launch &L, const int8_t *act, const
     a.a_pad = e.a_pad;
     a.beta_out = e.beta_out;
     a.scale_value = e.scale_value;
-    a.relu = e.relu;
+    a.neuron = e.neuron;
     a.out = out;
     a.acc_out = acc_out;
     a.bits_out = e.bits_out;

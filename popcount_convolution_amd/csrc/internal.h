@@ -42,11 +42,41 @@ __device__ __forceinline__ void store_through(T *p, T v)
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// The fused epilogue's output value: neuron(v * scale * beta + bias).
-__device__ __forceinline__ float epilogue_value(float v, float sc, float be, float bi, int relu)
+// The activation applied last: type (a bconv_neuron_t value) and parameters.
+struct Neuron {
+    int type;
+    float a, b;
+};
+constexpr int kNeuronNone = 0;
+constexpr int kNeuronRelu = 1;
+
+// neuron(r), in fp32 with the device math library (the definitions are listed
+// with bconv_neuron_t).
+__device__ __forceinline__ float apply_neuron(const Neuron &n, float r)
 {
-    const float r = __builtin_fmaf(v * sc, be, bi);
-    return relu ? ((r < 0.0f) ? 0.0f : r) : r;
+    switch (n.type) {
+    case 1: return (r < 0.0f) ? 0.0f : r;
+    case 2: return (r < 0.0f) ? n.a * r : r;
+    case 3: return __builtin_fmaf(n.a, r, n.b);
+    case 4: return 1.0f / (1.0f + expf(-r));
+    case 5: return fminf(fmaxf(__builtin_fmaf(n.a, r, n.b), 0.0f), 1.0f);
+    case 6: return n.a * tanhf(n.b * r);
+    case 7: return fabsf(r);
+    case 8: {
+        const float z = n.b * r;
+        return n.a * (fmaxf(z, 0.0f) + log1pf(expf(-fabsf(z))));
+    }
+    case 9: return r / (1.0f + fabsf(r));
+    case 10: return (r < 0.0f) ? n.a * expm1f(r) : r;
+    case 11: return fminf(fmaxf(r, n.a), n.b);
+    default: return r;
+    }
+}
+
+// The fused epilogue's output value: neuron(v * scale * beta + bias).
+__device__ __forceinline__ float epilogue_value(float v, float sc, float be, float bi, const Neuron &n)
+{
+    return apply_neuron(n, __builtin_fmaf(v * sc, be, bi));
 }
 
 // Sign bit of an output value, in the input encoding of the next binary
@@ -137,7 +167,7 @@ struct Epilogue {
     float scale_value;
     const float *a_pad;  // [n][bits_rows][bits_cols] or nullptr
     float *beta_out;     // [n][out_h][out_w] (used when a_pad is set)
-    int relu;
+    Neuron neuron;
     // Packed sign bits of the output instead of fp32 values: [n][out_h][out_w]
     // [out_words] words, channel c at bit c % 32 of word c / 32, bit = !(y < 0)
     // for the value y the fp32 output would hold, bits past out_c zero.

@@ -29,7 +29,7 @@ struct XArgs {
     const float *a_pad;  // zero-halo A map or nullptr (beta = 1)
     float *beta_out;
     float scale_value;
-    int relu;
+    Neuron neuron;
     float *out;
     int32_t *acc_out;
     uint32_t *bits_out;  // packed sign bits instead of out (see Epilogue)
@@ -58,9 +58,7 @@ __device__ __forceinline__ void store_result_buf(const XArgs &a, const __amdgpu_
     if (a.acc_out) {
         bitsv = (uint32_t)v;
     } else {
-        float r = __builtin_fmaf((float)v * sc, be, bi);
-        if (a.relu) r = (r < 0.0f) ? 0.0f : r;
-        bitsv = __builtin_bit_cast(uint32_t, r);
+        bitsv = __builtin_bit_cast(uint32_t, epilogue_value((float)v, sc, be, bi, a.neuron));
     }
     __builtin_amdgcn_raw_buffer_store_b32(bitsv, orr, (uint32_t)(co * 4), soff, kStoreSc1);
 }
@@ -76,9 +74,8 @@ __device__ __forceinline__ void store_result(const XArgs &a, long long pix, int 
         __hip_atomic_store(&a.acc_out[o], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return;
     }
-    float r = __builtin_fmaf((float)v * sc, be, bi);
-    if (a.relu) r = (r < 0.0f) ? 0.0f : r;
-    __hip_atomic_store(&a.out[o], r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&a.out[o], epilogue_value((float)v, sc, be, bi, a.neuron), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // v of lane i + N of the same 16-lane row (DPP row_shl:N; lanes past the row read 0).
@@ -304,7 +301,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void x
             if (ox >= a.out_w) break;
             const float be = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(be_lane), p));
             store_tile_bits(a.bits_out, ((long long)img * a.out_h + oy) * a.out_w + ox, a.out_words, (int)tile,
-                            co_ok && sign_bit(epilogue_value((float)window_value(p, ox), sc, be, bi, a.relu)));
+                            co_ok && sign_bit(epilogue_value((float)window_value(p, ox), sc, be, bi, a.neuron)));
         }
         return;
     }
@@ -324,13 +321,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void x
     };
     if (a.acc_out)
         store_all([](int v, float) { return (uint32_t)v; });
-    else if (a.relu)
+    else if (a.neuron.type == kNeuronRelu)
         store_all([&](int v, float be) {
             const float r = __builtin_fmaf((float)v * sc, be, bi);
             return __builtin_bit_cast(uint32_t, (r < 0.0f) ? 0.0f : r);
         });
-    else
+    else if (a.neuron.type == kNeuronNone)
         store_all([&](int v, float be) { return __builtin_bit_cast(uint32_t, __builtin_fmaf((float)v * sc, be, bi)); });
+    else
+        store_all([&](int v, float be) {
+            return __builtin_bit_cast(uint32_t, epilogue_value((float)v, sc, be, bi, a.neuron));
+        });
 }
 
 // Any geometry: one wave = one output pixel and a 64-channel tile; taps
@@ -384,7 +385,7 @@ __global__ __launch_bounds__(256) void xconv_generic(XArgs a, int and_mode)
         if (tile == 0 && lane == 0) a.beta_out[pix] = be;
     }
     if (a.bits_out)
-        store_tile_bits(a.bits_out, pix, a.out_words, (int)tile, co_ok && sign_bit(epilogue_value((float)v, sc, be, bi, a.relu)));
+        store_tile_bits(a.bits_out, pix, a.out_words, (int)tile, co_ok && sign_bit(epilogue_value((float)v, sc, be, bi, a.neuron)));
     else
         store_result(a, pix, co, v, sc, bi, be);
 }
@@ -474,7 +475,7 @@ XArgs make_args(const Geom &g, const uint32_t *bits, const LaneWeights &w, const
     a.a_pad = e.a_pad;
     a.beta_out = e.beta_out;
     a.scale_value = e.scale_value;
-    a.relu = e.relu;
+    a.neuron = e.neuron;
     a.out = out;
     a.acc_out = acc_out;
     a.bits_out = e.bits_out;

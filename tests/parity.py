@@ -124,8 +124,20 @@ def window_abs_sum(layer: workloads.Layer, inputs: dict) -> np.ndarray:
     return s.numpy()[:, 0]
 
 
+# Lipschitz constant of each activation (a, b its parameters), and whether its
+# fp32 evaluation rounds (then 1e-5 of the output is added to the bound).
+def _neuron_lipschitz(layer: workloads.Layer):
+    a, b = abs(layer.neuron_a), abs(layer.neuron_b)
+    return {"none": (1.0, False), "relu": (1.0, False), "absolute": (1.0, False), "clamp": (1.0, False),
+            "leaky_relu": (max(1.0, a), True), "linear": (a, True), "sigmoid": (0.25, True),
+            "hard_sigmoid": (a, True), "tanh": (a * b, True), "softplus": (a * b, True),
+            "softsign": (1.0, True), "elu": (max(1.0, a), True)}[layer.neuron]
+
+
 def output_bound(layer: workloads.Layer, sub: dict, ref: dict) -> np.ndarray:
-    """The normwise fp32 bound on each final output (see the module doc)."""
+    """The normwise fp32 bound on each final output (see the module doc),
+    carried through the activation: L * bound + 1e-5 * |out| for an
+    activation with Lipschitz constant L whose fp32 evaluation rounds."""
     oc = layer.out_c
     scale = (sub["output_scale"].astype(np.float64) if sub.get("output_scale") is not None
              else np.full(oc, layer.scale_value, np.float64))
@@ -134,8 +146,11 @@ def output_bound(layer: workloads.Layer, sub: dict, ref: dict) -> np.ndarray:
     beta = ref["beta"][..., None]
     if layer.type == "binary_weights":
         S = window_abs_sum(layer, sub)[..., None]
-        return RTOL * (np.abs(scale * beta) * S + np.abs(bias)) + TINY
-    return RTOL * (np.abs(ref["acc"] * scale * beta) + np.abs(bias)) + TINY
+        pre = RTOL * (np.abs(scale * beta) * S + np.abs(bias)) + TINY
+    else:
+        pre = RTOL * (np.abs(ref["acc"] * scale * beta) + np.abs(bias)) + TINY
+    lip, rounds = _neuron_lipschitz(layer)
+    return lip * pre + (RTOL * np.abs(ref["out"]) if rounds else 0.0)
 
 
 def unpack_words(words: np.ndarray, nbits: int) -> np.ndarray:
@@ -181,24 +196,17 @@ def compare(layer: workloads.Layer, inputs: dict, got: dict, ref: dict = None, i
         ref = oracle.bconv_layer(layer, sub)
     g = {k: (v if images is None or not isinstance(v, np.ndarray) else v[images])
          for k, v in got.items()}
-    oc = layer.out_c
-    scale = (sub["output_scale"].astype(np.float64) if sub.get("output_scale") is not None
-             else np.full(oc, layer.scale_value, np.float64))
-    bias = (sub["output_bias"].astype(np.float64) if sub.get("output_bias") is not None
-            else np.zeros(oc))
-    beta = ref["beta"][..., None]
     if layer.type == "binary_weights":
         S = window_abs_sum(layer, sub)[..., None]
         err = np.abs(g["acc"].astype(np.float64) - ref["acc"])
         assert np.all(err <= RTOL * S + TINY), f"{layer.name}: binaryWeights sums off by {err.max()}"
-        bound = RTOL * (np.abs(scale * beta) * S + np.abs(bias)) + TINY
     else:
         if not np.array_equal(g["acc"], ref["acc"]):
             bad = np.argwhere(g["acc"] != ref["acc"])
             i = tuple(bad[0])
             raise AssertionError(f"{layer.name}: {len(bad)} window sums differ, first at {i}: "
                                  f"gpu {g['acc'][i]} oracle {ref['acc'][i]}")
-        bound = RTOL * (np.abs(ref["acc"] * scale * beta) + np.abs(bias)) + TINY
+    bound = output_bound(layer, sub, ref)
     err = np.abs(g["out"].astype(np.float64) - ref["out"])
     ok = err <= bound
     if not np.all(ok):

@@ -58,7 +58,9 @@ def _desc(**kw):
     ({}, pca.BCONV_AND, pca.BCONV_FLAG_INT8_MFMA | 1, pca.BCONV_OK),
     ({}, pca.BCONV_BINARY_WEIGHTS, pca.BCONV_FLAG_INT8_MFMA, pca.BCONV_ERR_INVALID_ARGUMENT),
     ({}, pca.BCONV_XNOR, 4, pca.BCONV_ERR_INVALID_ARGUMENT),
-    (dict(neuron=2), pca.BCONV_XNOR, 0, pca.BCONV_ERR_INVALID_ARGUMENT),
+    (dict(neuron=11, neuron_a=-1.0, neuron_b=1.0), pca.BCONV_XNOR, 0, pca.BCONV_OK),  # clamp
+    (dict(neuron=12), pca.BCONV_XNOR, 0, pca.BCONV_ERR_INVALID_ARGUMENT),
+    (dict(neuron=-1), pca.BCONV_XNOR, 0, pca.BCONV_ERR_INVALID_ARGUMENT),
     (dict(in_h=0), pca.BCONV_XNOR, 0, pca.BCONV_ERR_INVALID_ARGUMENT),
     (dict(in_c=-1), pca.BCONV_XNOR, 0, pca.BCONV_ERR_INVALID_ARGUMENT),
     (dict(out_c=0), pca.BCONV_XNOR, 0, pca.BCONV_ERR_INVALID_ARGUMENT),

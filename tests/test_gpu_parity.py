@@ -182,6 +182,47 @@ def test_binary_weights_special_values(dev):
         assert np.any(g[1] != 0) and np.any(g[2] != 0), "tiny values must not flush to zero"
 
 
+# ------------------------------------------------------------ activations
+
+NEURON_PARAMS = {"leaky_relu": (0.1, 0.0), "linear": (0.5, -0.25), "sigmoid": (0.0, 0.0),
+                 "hard_sigmoid": (0.2, 0.5), "tanh": (1.5, 0.7), "absolute": (0.0, 0.0),
+                 "softplus": (0.8, 1.3), "softsign": (0.0, 0.0), "elu": (0.6, 0.0), "clamp": (-0.5, 0.75),
+                 "relu": (0.0, 0.0), "none": (0.0, 0.0)}
+
+
+def _neuron_layers():
+    # output scale ~0.01 so the values sit in every activation's curved range
+    xnor = workloads.Layer("act", "xnor", 2, 9, 10, 64, 70, 3, 3, 1, 1, 1, 1,
+                           oscale_dist=("uniform", 0.002, 0.02), obias_dist=("normal", 0.0, 1.0))
+    bw = xnor.with_(type="binary_weights", in_c=24, oscale_dist=("uniform", 0.1, 0.5))
+    out = []
+    for name, (a, b) in NEURON_PARAMS.items():
+        out.append(xnor.with_(name=f"act_xnor_{name}", neuron=name, neuron_a=a, neuron_b=b))
+        out.append(bw.with_(name=f"act_bw_{name}", neuron=name, neuron_a=a, neuron_b=b))
+    return out
+
+
+NEURON_LAYERS = _neuron_layers()
+
+
+@pytest.mark.parametrize("layer", NEURON_LAYERS, ids=[l.name for l in NEURON_LAYERS])
+def test_neuron(dev, layer):
+    """Every activation through the specialised and generic kernels (and the
+    int8 path for XNOR), fp32 outputs and sign bits."""
+    inputs = workloads.make_inputs(layer, 9500 + NEURON_LAYERS.index(layer))
+    _log(f"neuron {layer}")
+    ref = oracle.bconv_layer(layer, inputs)
+    variants = [dict(generic=False), dict(generic=True)]
+    if layer.type != "binary_weights":
+        variants.append(dict(int8_mfma=True))
+    for v in variants:
+        got = parity.run_gpu(layer, inputs, dev, **v)
+        parity.compare(layer, inputs, got, ref=ref)
+    words, out, kernel = _run_bits(layer, inputs, dev)
+    assert np.array_equal(parity.unpack_words(words, layer.out_c), (~(out < 0)).astype(np.uint8)), kernel
+    parity.compare_bits(layer, inputs, words, ref=ref)
+
+
 # ------------------------------------------------ asymmetric padding
 
 def _pad_layers():
