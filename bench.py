@@ -16,7 +16,9 @@ HBM.  Prints one JSON line:
              roofline against the dense int8 MFMA peak or HBM; and the layer
              with its output written as packed sign bits for a next binary
              layer (bconv_forward_bits), timed the same way;
-  cpu_baseline  the CPU oracle timed on a bounded sample of the same layer.
+  cpu_baseline  the CPU oracle timed on a bounded sample of the same layer;
+  cpu_packed_baseline  (XNOR / AND) the packed-bit popcount form on the CPU
+             (the oracle package's second reference point), whole batch.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layer I]
 """
@@ -122,6 +124,23 @@ def cpu_baseline(layer, inputs, images: int, repeats: int):
             else "GMAC/s (fp32)", "cores": threads, "kind": "oracle",
             "sample": f"{images} of {layer.n} images of {layer.name}, best of {repeats} runs "
                       f"({best:.3f} s each, {macs} nominal MACs)"}
+
+
+def cpu_packed_baseline(layer, inputs, repeats: int):
+    """Time the packed-bit popcount CPU baseline on the whole batch, all host cores."""
+    import oracle
+    threads = os.cpu_count() or 1
+    oracle.load_packed()
+    best = None
+    for _ in range(max(1, repeats)):
+        t = time.perf_counter()
+        oracle.packed_bconv(layer, inputs, threads=threads)
+        dt = time.perf_counter() - t
+        best = dt if best is None else min(best, dt)
+    macs = layer.nominal_macs()
+    return {"value": macs / best / 1e9, "unit": "GOPS (bit-MAC/s)", "cores": threads,
+            "kind": "packed popcount CPU (oracle/packed_cpu.c)",
+            "sample": f"all {layer.n} images of {layer.name}, best of {repeats} runs ({best * 1e3:.3f} ms each)"}
 
 
 def main():
@@ -242,6 +261,8 @@ def main():
                          "frac": round(rb[1] / rb[2], 4), "algorithmic_bytes": nbb}}
     if args.cpu_images > 0:
         line["cpu_baseline"] = cpu_baseline(layer, inputs, min(args.cpu_images, n), args.cpu_repeats)
+        if binary and layer.neuron in ("none", "relu"):
+            line["cpu_packed_baseline"] = cpu_packed_baseline(layer, inputs, args.cpu_repeats)
     else:
         line["cpu_baseline"] = None
     conv.close()

@@ -8,6 +8,11 @@ evaluation of the output equation of Apple's "MPSCNNBinaryConvolution" page
 layer to (kernel = source size, stride 1, output 1x1).
 
 ``bconv(...)`` builds ``liboracle.so`` with gcc on first use if it is missing.
+
+``packed_bconv(...)`` is a second CPU reference point for throughput, not a
+checker: the packed-bit popcount form of XNOR / AND on the CPU
+(``packed_cpu.c``), itself checked against ``bconv`` by the tests.  The same
+import rule applies to it.
 """
 
 from __future__ import annotations
@@ -29,7 +34,11 @@ NEURON_CODES = {"none": 0, "relu": 1,
                 "hard_sigmoid": 5, "tanh": 6, "absolute": 7, "softplus": 8,
                 "softsign": 9, "elu": 10, "clamp": 11}
 
+_PACKED_SRC = os.path.join(_HERE, "packed_cpu.c")
+_PACKED_LIB = os.path.join(_HERE, "libpacked_cpu.so")
+
 _lib = None
+_packed = None
 
 
 def build(src: str = _SRC, out: str = _LIB, extra_flags=()) -> str:
@@ -60,6 +69,54 @@ def load(path: Optional[str] = None):
     if path is None:
         _lib = lib
     return lib
+
+
+def build_packed(out: str = _PACKED_LIB) -> str:
+    """Compile the packed CPU baseline with gcc (-O3, OpenMP, hardware popcount)."""
+    cmd = ["gcc", "-std=c11", "-O3", "-mpopcnt", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+           _PACKED_SRC, "-o", out + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def load_packed():
+    global _packed
+    if _packed is not None:
+        return _packed
+    if not os.path.exists(_PACKED_LIB) or os.path.getmtime(_PACKED_LIB) < os.path.getmtime(_PACKED_SRC):
+        build_packed()
+    lib = ctypes.CDLL(_PACKED_LIB)
+    i, f, vp = ctypes.c_int, ctypes.c_float, ctypes.c_void_p
+    lib.packed_bconv.restype = i
+    lib.packed_bconv.argtypes = [i] * 16 + [f] + [vp] * 8 + [i]
+    _packed = lib
+    return lib
+
+
+def packed_bconv(layer, inputs: dict, threads: int = 0, images=None) -> dict:
+    """The packed-bit CPU baseline on a ``workloads.Layer`` (XNOR / AND,
+    neuron none or ReLU): fp32 ``out`` and int32 ``acc``."""
+    lib = load_packed()
+    x = inputs["x"] if images is None else inputs["x"][images]
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    n = x.shape[0]
+    out = np.empty((n, layer.out_h, layer.out_w, layer.out_c), np.float32)
+    acc = np.empty(out.shape, np.int32)
+
+    def f32(a):
+        return None if a is None else np.ascontiguousarray(a, dtype=np.float32)
+
+    keep = [f32(inputs.get(k)) for k in ("output_scale", "output_bias", "input_scale", "input_bias")]
+    wb = np.ascontiguousarray(inputs["weight_bits"], dtype=np.uint32)
+    rc = lib.packed_bconv(n, layer.in_h, layer.in_w, layer.in_c, layer.out_c, layer.kernel_h, layer.kernel_w,
+                          layer.stride_h, layer.stride_w, layer.pad_h, layer.pad_w, layer.pad_h_end, layer.pad_w_end,
+                          TYPE_CODES[layer.type], int(bool(layer.use_beta)), NEURON_CODES[layer.neuron],
+                          float(layer.scale_value), _ptr(x), _ptr(wb), *[_ptr(k) for k in keep], _ptr(out),
+                          _ptr(acc), int(threads))
+    if rc != 0:
+        raise ValueError("packed CPU baseline: arguments outside its scope")
+    return {"out": out, "acc": acc}
 
 
 def _ptr(a):
