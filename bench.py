@@ -21,6 +21,8 @@ HBM.  Prints one JSON line:
              (the oracle package's second reference point), whole batch.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layer I]
+       python bench.py --sweep   (geometry sweep around the bench layer: strides,
+                                  paddings, odd and even kernels; one JSON line)
 """
 
 from __future__ import annotations
@@ -94,6 +96,10 @@ def parse():
     p.add_argument("--cpu-repeats", type=int, default=3)
     p.add_argument("--no-int8", action="store_true",
                    help="skip the int8 matrix-core comparison (XNOR / AND layers)")
+    p.add_argument("--sweep", action="store_true",
+                   help="time the convolution over a sweep of strides, paddings and kernel sizes")
+    p.add_argument("--sweep-widths", action="store_true",
+                   help="with --sweep: also time every strip width of the specialised convolution")
     p.add_argument("--no-bits", action="store_true",
                    help="skip the packed sign-bit output comparison")
     p.add_argument("--profile-only", action="store_true",
@@ -143,6 +149,64 @@ def cpu_packed_baseline(layer, inputs, repeats: int):
             "sample": f"all {layer.n} images of {layer.name}, best of {repeats} runs ({best * 1e3:.3f} ms each)"}
 
 
+def sweep_layers(workloads):
+    """Geometries around the bench layer (XNOR + beta + affine + ReLU, batch 8,
+    128 -> 128 channels): strides 1 and 2, paddings none / centred, kernels
+    1, 2, 3, 4, 5 (even ones with the centred window's asymmetric padding)."""
+    base = workloads.BENCH_LAYER
+    out = []
+    for k in (1, 2, 3, 4, 5):
+        for s in (1, 2):
+            for centred in (True, False):
+                if k == 1 and not centred:
+                    continue
+                p, pe = (k // 2, (k - 1) // 2) if centred else (0, 0)
+                name = f"xnor_beta_b8_56x56_c128_o128_k{k}_s{s}_p{p}{'' if pe == p else f'-{pe}'}"
+                out.append(base.with_(name=name, kernel_h=k, kernel_w=k, stride_h=s, stride_w=s, pad_h=p, pad_w=p,
+                                      pad_bottom=pe, pad_right=pe))
+    return out
+
+
+def run_sweep(args):
+    import numpy as np
+    import torch
+
+    import popcount_convolution_amd as pca
+    from popcount_convolution_amd import workloads
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream()
+    rows = []
+    # BCONV_STRIP_WIDTH (read when a handle is created) forces the strip width
+    widths = (0, 4, 6, 7, 8) if args.sweep_widths else (0,)
+    for i, layer in enumerate(sweep_layers(workloads)):
+        inputs = workloads.make_inputs(layer, 4000 + i)
+        x = torch.from_numpy(inputs["x"]).to(dev)
+        for width in widths:
+            os.environ["BCONV_STRIP_WIDTH"] = str(width)
+            conv = pca.BinaryConvolution.from_layer(layer, inputs)
+            os.environ.pop("BCONV_STRIP_WIDTH")
+            kernel = conv.main_kernel(layer.n)
+            if width and not kernel.endswith(f",{width}>"):
+                conv.close()
+                continue
+            ms, main_ms, out = time_path(pca, torch, np, conv, layer.n, x, stream, args.warmup, args.steps)
+            macs = layer.nominal_macs()
+            achieved = macs / (main_ms / 1e3) / 1e12
+            rows.append({"workload": layer.name, "strip_width": width or "auto", "kernel": kernel,
+                         "out_hw": [layer.out_h, layer.out_w], "avg_kernel_us": round(main_ms * 1e3, 3),
+                         "ms_per_step": round(ms, 6), "value": round(macs / (ms / 1e3) / 1e9, 3),
+                         "achieved": round(achieved, 3), "frac": round(achieved / POPCOUNT_PEAK_TBITMAC, 4)})
+            print(f"# {layer.name}: {kernel} {rows[-1]['avg_kernel_us']} us, frac {rows[-1]['frac']}",
+                  file=sys.stderr, flush=True)
+            del out
+            conv.close()
+    print(json.dumps({"metric": "binary conv GOPS (bit-MACs/s) over a geometry sweep, 1 MI355X",
+                      "unit": "GOPS (bit-MAC/s)", "peak_unit": "Tbit-MAC/s", "peak": POPCOUNT_PEAK_TBITMAC,
+                      "steps": args.steps, "warmup": args.warmup, "n_gpus": 1, "data": "synthetic", "sweep": rows}),
+          flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -159,6 +223,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.sweep:
+        run_sweep(args)
+        return
     index = workloads.LAYERS.index(workloads.BENCH_LAYER) if args.layer is None else args.layer
     layer = workloads.LAYERS[index]
     inputs = workloads.make_inputs(layer, workloads.layer_seed(index))
@@ -311,9 +378,9 @@ def time_path(pca, torch, np, conv, n, x, stream, warmup, steps, bits=False):
     return t0.elapsed_time(t1) / steps, main_ms, out
 
 
-# the source file that defines (and launches) each main kernel
-KERNEL_FILES = {"xconv": "xconv.hip", "bgemm": "gemm.hip", "bwmma": "bwmma.hip", "bwconv": "bwconv.hip",
-                "i8mma": "i8mma.hip"}
+# the source file that defines (and launches) each main kernel, by name prefix
+KERNEL_FILES = {"xconv_fast": "xconv_fast.h", "xconv_generic": "xconv.hip", "bgemm": "gemm.hip",
+                "bwmma": "bwmma.hip", "bwconv": "bwconv.hip", "i8mma": "i8mma.hip"}
 
 
 def _kernel_sha(kernel: str) -> str:
@@ -322,7 +389,8 @@ def _kernel_sha(kernel: str) -> str:
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "popcount_convolution_amd", "csrc")
-    prefix = kernel.split("<")[0].split("_")[0]
+    base = kernel.split("<")[0]
+    prefix = next(p for p in KERNEL_FILES if base.startswith(p))
     for name in (KERNEL_FILES[prefix], "internal.h"):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())

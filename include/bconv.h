@@ -171,7 +171,15 @@ bconv_status_t bconv_validate_desc(const bconv_desc_t *desc, int32_t type, uint3
  * Every array is copied; the caller keeps ownership of its buffers.  The
  * weights are rearranged on the device into the layouts the kernels read.
  * Synchronous.  On success *out receives a handle to release with
- * bconv_destroy. */
+ * bconv_destroy.
+ * Two environment variables, read here, fix the kernel choice of the handle
+ * (for tests and tuning; results do not depend on them):
+ *   BCONV_FORCE_GENERIC=1  the shape-generic kernels instead of the
+ *                          specialised and matrix routes;
+ *   BCONV_STRIP_WIDTH=P    the specialised XNOR / AND convolution processes P
+ *                          output pixels per wave when a kernel for that width
+ *                          is compiled for the shape (otherwise the width is
+ *                          chosen by cost). */
 bconv_status_t bconv_create(const bconv_desc_t *desc, const uint32_t *weight_bits,
                             const float *output_scale, const float *output_bias,
                             const float *input_scale, const float *input_bias, int32_t type,

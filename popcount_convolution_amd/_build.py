@@ -17,7 +17,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbconv.so")
-SOURCES = ("bconv.hip", "pack.hip", "prepack.hip", "xconv.hip", "bwconv.hip", "bwmma.hip", "gemm.hip", "i8mma.hip")
+# longest compiles first, so they start before the pool fills
+SOURCES = ("xconv_k3.hip", "xconv_k24.hip", "xconv_k5.hip", "xconv_k1.hip", "bwmma.hip", "i8mma.hip", "gemm.hip",
+           "xconv.hip", "bwconv.hip", "bconv.hip", "pack.hip", "prepack.hip")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

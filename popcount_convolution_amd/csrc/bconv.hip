@@ -22,6 +22,7 @@ struct bconv_handle {
     int out_h, out_w, words, tiles;
     int simds;                // SIMD units of the device
     bool force_generic;
+    int strip_width;          // forced strip width of the specialised convolution (0: by cost)
     bconv::LaneWeights lane;  // XNOR / AND
     uint32_t *d_lane_words;
     int32_t *d_lane_popc;
@@ -116,6 +117,7 @@ bconv::Geom make_geom(const bconv_handle *h, int n)
     g.words = h->words;
     g.tiles = h->tiles;
     g.simds = h->simds;
+    g.strip_p = h->strip_width;
     g.bits_halo_h = d.pad_h;
     g.bits_halo_w = d.pad_w;
     g.bits_rows = d.in_h + d.pad_h + d.pad_h_end;
@@ -329,6 +331,8 @@ bconv_status_t bconv_create(const bconv_desc_t *desc, const uint32_t *weight_bit
     h->tiles = (desc->out_c + bconv::kTile - 1) / bconv::kTile;
     const char *fg = getenv("BCONV_FORCE_GENERIC");
     h->force_generic = fg && fg[0] == '1';
+    const char *sp = getenv("BCONV_STRIP_WIDTH");
+    h->strip_width = sp ? atoi(sp) : 0;
     hipError_t e = hipGetDevice(&h->device);
     int cus = 0;
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h->device);

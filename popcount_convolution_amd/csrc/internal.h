@@ -22,11 +22,12 @@ struct Geom {
     int words;        // ceil(in_c / 32)
     int tiles;        // ceil(out_c / kTile)
     // binarised-input buffer with a zero halo
-    int bits_rows;    // in_h + 2*ph
-    int bits_cols;    // in_w + 2*pw
+    int bits_rows;    // in_h + ph + trailing pad
+    int bits_cols;    // in_w + pw + trailing pad
     int bits_halo_h, bits_halo_w;
     long long bits_slack_words;  // zero words after the last image (strip over-reads)
     int simds;        // SIMD units of the device (4 per compute unit)
+    int strip_p;      // strip width the specialised convolution must use (0: by cost)
 };
 
 // Raw buffer descriptor word 3 for gfx9-family targets (32-bit data format).

@@ -1,0 +1,18 @@
+// Compiled instances of the specialised XNOR / AND convolution kernel for
+// 5x5 windows: (KH, KW, words per pixel, horizontal stride) at each strip width.
+#include "xconv_fast.h"
+
+namespace bconv {
+namespace {
+
+const FastEntry kTable[] = {
+    BCONV_FAST_P(5, 5, 1, 1), BCONV_FAST_P(5, 5, 2, 1), BCONV_FAST_P(5, 5, 4, 1),
+    // stride 2
+    BCONV_FAST_P(5, 5, 1, 2), BCONV_FAST_P(5, 5, 2, 2), BCONV_FAST_P(5, 5, 4, 2),
+};
+
+}  // namespace
+
+FastTable xconv_fast_k5() { return {kTable, (int)(sizeof(kTable) / sizeof(kTable[0]))}; }
+
+}  // namespace bconv

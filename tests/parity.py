@@ -29,17 +29,20 @@ TINY = 1e-30
 
 
 @contextmanager
-def force_generic(on: bool):
-    """Handles created inside use the generic convolution kernel."""
-    old = os.environ.get("BCONV_FORCE_GENERIC")
-    os.environ["BCONV_FORCE_GENERIC"] = "1" if on else "0"
+def force_generic(on: bool, strip_width: int = 0):
+    """Handles created inside use the generic convolution kernel, or the
+    specialised one at the given strip width (0: chosen by cost)."""
+    values = {"BCONV_FORCE_GENERIC": "1" if on else "0", "BCONV_STRIP_WIDTH": str(strip_width)}
+    old = {k: os.environ.get(k) for k in values}
+    os.environ.update(values)
     try:
         yield
     finally:
-        if old is None:
-            os.environ.pop("BCONV_FORCE_GENERIC", None)
-        else:
-            os.environ["BCONV_FORCE_GENERIC"] = old
+        for k, v in old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
 
 
 def slice_inputs(inputs: dict, images) -> dict:
@@ -49,11 +52,12 @@ def slice_inputs(inputs: dict, images) -> dict:
 
 
 def run_gpu(layer: workloads.Layer, inputs: dict, device, generic: bool = False,
-            int8_mfma: bool = False) -> dict:
+            int8_mfma: bool = False, strip_width: int = 0) -> dict:
     """Forward and forward_accum through the C ABI; also returns the
     workspace intermediates (bits or int8 values, A map, beta) of the forward
-    call.  ``int8_mfma`` selects the int8 matrix-core comparison path."""
-    with force_generic(generic):
+    call.  ``int8_mfma`` selects the int8 matrix-core comparison path;
+    ``strip_width`` forces the specialised convolution's pixels per wave."""
+    with force_generic(generic, strip_width):
         conv = pca.BinaryConvolution.from_layer(layer, inputs, int8_mfma=int8_mfma)
     try:
         n = inputs["x"].shape[0]

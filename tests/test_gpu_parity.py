@@ -127,6 +127,49 @@ def test_sweep(dev, layer):
     parity.compare(layer, inputs, gen, ref=ref)
 
 
+# ------------------------------------------------------- specialised kernels
+
+# (kernel_h, kernel_w, words per pixel, stride) of every compiled instance of
+# the specialised XNOR / AND convolution, and its strip widths.
+FAST_SHAPES = ([(3, 3, cw, 1) for cw in (1, 2, 3, 4, 8)] + [(3, 3, cw, 2) for cw in (1, 2, 4, 8)]
+               + [(1, 1, cw, s) for s in (1, 2) for cw in (1, 2, 4, 8)]
+               + [(k, k, cw, s) for k in (2, 4, 5) for s in (1, 2) for cw in (1, 2, 4)])
+STRIP_WIDTHS = (4, 6, 7, 8)
+
+
+def _fast_layer(kh, kw, cw, sw, p, form, variant):
+    """Two images, two channel tiles (the second ragged), a ragged last word,
+    centred padding (an even kernel pads one less at the end) and rows of
+    two whole strips of width p plus a ragged one."""
+    ph, pw = kh // 2, kw // 2
+    out_w = 2 * p + 3
+    in_w = (out_w - 1) * sw + kw - pw - (kw - 1 - pw)
+    kwargs = dict(name=f"k{kh}x{kw}_w{cw}_s{sw}_p{p}_{form}_v{variant}", type=form, n=2, in_h=7, in_w=in_w,
+                  in_c=32 * cw - 5 if cw > 1 else 27, out_c=70, kernel_h=kh, kernel_w=kw,
+                  stride_h=sw, stride_w=sw, pad_h=ph, pad_w=pw, pad_bottom=kh - 1 - ph, pad_right=kw - 1 - pw)
+    if variant:
+        kwargs.update(use_beta=True, neuron="relu", iscale_dist=("uniform", 0.5, 1.5),
+                      ibias_dist=("normal", 0.0, 0.2))
+    return workloads.Layer(**kwargs)
+
+
+@pytest.mark.parametrize("shape", FAST_SHAPES, ids=["k{}x{}_w{}_s{}".format(*s) for s in FAST_SHAPES])
+def test_fast_kernel_instances(dev, shape):
+    """Every compiled instance (each strip width, XNOR and AND, with and
+    without beta / input affine / ReLU) matches the oracle on a layer with
+    borders on all sides and ragged strips, tiles and words."""
+    kh, kw, cw, sw = shape
+    for i, p in enumerate(STRIP_WIDTHS):
+        for j, form in enumerate(("xnor", "and")):
+            layer = _fast_layer(kh, kw, cw, sw, p, form, (i + j) % 2)
+            assert layer.out_w == 2 * p + 3 and (layer.in_c + 31) // 32 == cw
+            inputs = workloads.make_inputs(layer, 9000 + 8 * FAST_SHAPES.index(shape) + 2 * i + j)
+            _log(f"fast {layer}")
+            got = parity.run_gpu(layer, inputs, dev, strip_width=p)
+            assert got["main_kernel"] == f"xconv_fast<{kh},{kw},{cw},{sw},{p}>"
+            parity.compare(layer, inputs, got)
+
+
 def test_special_values(dev):
     """Signed zeros, NaN, subnormals and exact ties of the input affine
     binarise as the oracle says (x' < 0 -> -1, else +1)."""
