@@ -46,7 +46,7 @@ struct XArgs {
     int kwc4, tiles;
     int strips_per_row;
     long long strips;
-    FastDiv div_tiles, div_spr, div_oh;  // by tiles, strips_per_row, out_h
+    FastDiv div_tiles, div_oh, div_img;  // by tiles, out_h, strips_per_row * out_h
     // buffer sizes in bytes (each < 2^31, checked by the host)
     int out_bytes, wlane_bytes, wrect_bytes, apad_bytes, beta_bytes;
 };
@@ -108,7 +108,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void x
     // Workgroups are dealt to the eight XCDs round-robin (block b to XCD
     // b % 8); renumbering gives XCD x a contiguous run of strips, so its L2
     // fetches only the input rows of its own part of the batch.  The grid is
-    // a multiple of 8 blocks; blocks past the work exit below.
+    // a multiple of 8 blocks; blocks past the work exit below.  Strips are
+    // numbered down the columns of an image: consecutive strips (a
+    // workgroup's, and those dealt to neighbouring CUs at the same time) are
+    // vertical neighbours that share KH - 1 of their input rows in the caches.
     const int lane = threadIdx.x & 63;
     const unsigned per_xcd = gridDim.x >> 3;
     const unsigned blk = (blockIdx.x & 7u) * per_xcd + (blockIdx.x >> 3);
@@ -118,11 +121,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void x
     const unsigned tile = gw - strip * (unsigned)a.tiles;
     if (strip >= (unsigned)a.strips) return;
 
-    const unsigned row = fastdiv(strip, a.div_spr);
-    const int ow0 = (int)(strip - row * (unsigned)a.strips_per_row) * P;
-    const unsigned imgu = fastdiv(row, a.div_oh);
+    const unsigned imgu = fastdiv(strip, a.div_img);
+    const unsigned in_img = strip - imgu * (unsigned)(a.strips_per_row * a.out_h);
+    const unsigned col = fastdiv(in_img, a.div_oh);
+    const int ow0 = (int)col * P;
     const int img = (int)imgu;
-    const int oy = (int)(row - imgu * (unsigned)a.out_h);
+    const int oy = (int)(in_img - col * (unsigned)a.out_h);
 
     // beta of pixel `lane` (lanes < P): window sum of the zero-halo A map.
     // Consumed in the epilogue.
@@ -336,8 +340,8 @@ hipError_t launch_fast(XArgs a, const Launch &L, int and_mode)
     a.strips_per_row = (a.out_w + P - 1) / P;
     a.strips = (long long)a.n * a.out_h * a.strips_per_row;
     a.div_tiles = make_fastdiv((uint32_t)a.tiles);
-    a.div_spr = make_fastdiv((uint32_t)a.strips_per_row);
     a.div_oh = make_fastdiv((uint32_t)a.out_h);
+    a.div_img = make_fastdiv((uint32_t)(a.strips_per_row * a.out_h));
     const long long waves = a.strips * a.tiles;
     const long long blocks = ((waves + 3) / 4 + 7) / 8 * 8;  // a multiple of the 8 XCDs
     if (blocks * 4 * 4 >= 0x7fffffffLL) return hipErrorInvalidValue;

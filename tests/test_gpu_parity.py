@@ -441,6 +441,46 @@ def test_repeat_is_bit_identical(dev):
     assert np.array_equal(a["beta"].view(np.uint32), b["beta"].view(np.uint32))
 
 
+REUSE_LAYERS = [workloads.BENCH_LAYER.with_(n=2), workloads.LAYERS[2].with_(n=2),
+                 workloads.LAYERS[3].with_(n=2), workloads.LAYERS[4].with_(n=5)]
+
+
+@pytest.mark.parametrize("layer", REUSE_LAYERS, ids=[l.name for l in REUSE_LAYERS])
+def test_new_input_reuses_workspace(dev, layer):
+    """One handle and one workspace, two different inputs in turn (forward,
+    forward_accum and the event-bracketed forward): every call matches the
+    oracle on its own input, so nothing of an earlier call's packed input, A
+    map or beta survives into a later one."""
+    inputs = [workloads.make_inputs(layer, 21)]
+    inputs.append(dict(inputs[0], x=workloads.make_inputs(layer, 22)["x"]))
+    refs = [oracle.bconv_layer(layer, inp) for inp in inputs]
+    conv = pca.BinaryConvolution.from_layer(layer, inputs[0])
+    try:
+        n = layer.n
+        ws = conv.workspace(n, dev)
+        xs = [torch.from_numpy(inp["x"]).to(dev) for inp in inputs]
+        shape = (n, conv.out_h, conv.out_w, conv.out_c)
+        acc_dtype = torch.float32 if layer.type == "binary_weights" else torch.int32
+        begin, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        begin.record(), end.record()
+        for rnd in range(3):
+            for k in (0, 1):
+                out = torch.full(shape, float("nan"), dtype=torch.float32, device=dev)
+                acc = torch.zeros(shape, dtype=acc_dtype, device=dev)
+                conv.forward_accum(xs[k], acc, ws)
+                if rnd == 1:
+                    pca.bconv_forward_profiled(conv.handle, torch.cuda.current_stream().cuda_stream, n, xs[k], out,
+                                               ws, ws.numel(), begin.cuda_event, end.cuda_event)
+                else:
+                    conv.forward(xs[k], out, ws)
+                torch.cuda.synchronize()
+                _log(f"reuse {layer.name} round {rnd} input {k}")
+                parity.compare(layer, inputs[k], {"out": out.cpu().numpy(), "acc": acc.cpu().numpy()}, ref=refs[k],
+                               workspace=False)
+    finally:
+        conv.close()
+
+
 def test_two_streams_share_a_handle(dev):
     layer = workloads.LAYERS[2].with_(n=4)
     inputs = workloads.make_inputs(layer, 4)
