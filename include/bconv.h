@@ -39,7 +39,10 @@
  *     subnormals are kept.
  *   - beta[i,y,x] = (sum of A over the window's in-image taps)/(kernel_h *
  *     kernel_w), A[i,y,x] = sum_f |in'[i,y,x,f]| / in_c; beta = 1 without
- *     BCONV_FLAG_USE_BETA_SCALING.  It applies to all three forms.
+ *     BCONV_FLAG_USE_BETA_SCALING.  It applies to all three forms.  With
+ *     BCONV_FLAG_BETA_VALID_TAPS as well, the divisor is instead the number
+ *     of the window's in-image taps (a mean of A over the image part of the
+ *     window, so beta stays |c| at the borders for a constant input c).
  *   - A missing output scale array means the scalar desc.scale_value; missing
  *     biases mean 0; a missing input scale means 1.
  *   - neuron: one of bconv_neuron_t, applied last; ReLU is r < 0 ? 0 : r.
@@ -89,11 +92,16 @@ typedef enum {
  * with int32 accumulation.  Results are identical (exact integers, the same
  * fp32 epilogue).  The workspace's bits section then holds those int8 values,
  * channels padded with 0 to a multiple of 64, four per uint32 word
- * (bits_words = padded channels / 4).  Not valid with BCONV_BINARY_WEIGHTS. */
+ * (bits_words = padded channels / 4).  Not valid with BCONV_BINARY_WEIGHTS.
+ * BCONV_FLAG_BETA_VALID_TAPS divides beta's window sum by the count of
+ * in-image taps instead of kernel_h * kernel_w (the other reading of the
+ * divisor of the page's first beta equation where the window leaves the
+ * image; identical inside the image).  Requires BCONV_FLAG_USE_BETA_SCALING. */
 enum {
     BCONV_FLAG_NONE = 0u,
     BCONV_FLAG_USE_BETA_SCALING = 1u,
-    BCONV_FLAG_INT8_MFMA = 2u
+    BCONV_FLAG_INT8_MFMA = 2u,
+    BCONV_FLAG_BETA_VALID_TAPS = 4u
 };
 
 /* The activation applied last (MPSCNNBinaryConvolution, Overview, closing

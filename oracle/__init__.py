@@ -111,7 +111,8 @@ def packed_bconv(layer, inputs: dict, threads: int = 0, images=None) -> dict:
     wb = np.ascontiguousarray(inputs["weight_bits"], dtype=np.uint32)
     rc = lib.packed_bconv(n, layer.in_h, layer.in_w, layer.in_c, layer.out_c, layer.kernel_h, layer.kernel_w,
                           layer.stride_h, layer.stride_w, layer.pad_h, layer.pad_w, layer.pad_h_end, layer.pad_w_end,
-                          TYPE_CODES[layer.type], int(bool(layer.use_beta)), NEURON_CODES[layer.neuron],
+                          TYPE_CODES[layer.type], 0 if not layer.use_beta else (2 if layer.beta_valid_taps else 1),
+                          NEURON_CODES[layer.neuron],
                           float(layer.scale_value), _ptr(x), _ptr(wb), *[_ptr(k) for k in keep], _ptr(out),
                           _ptr(acc), int(threads))
     if rc != 0:
@@ -132,7 +133,7 @@ def bconv(x: np.ndarray, weight_bits: np.ndarray, *, type: str, out_c: int,
           kernel=(1, 1), stride=(1, 1), pad=(0, 0), pad_end=None, output_scale=None, output_bias=None,
           input_scale=None, input_bias=None, use_beta: bool = False, neuron: str = "none",
           scale_value: float = 1.0, neuron_a: float = 0.0, neuron_b: float = 0.0, threads: int = 0,
-          want=("out", "acc", "beta", "a_map", "signs"),
+          want=("out", "acc", "beta", "a_map", "signs"), beta_divisor: str = "window",
           lib=None) -> dict:
     """Evaluate binary convolution on the CPU.
 
@@ -142,7 +143,12 @@ def bconv(x: np.ndarray, weight_bits: np.ndarray, *, type: str, out_c: int,
     Returns a dict of float64 ``out``, the pre-epilogue sum ``acc`` (int32 for
     XNOR/AND, float64 for binary_weights), ``beta`` [n,oh,ow], ``a_map``
     [n,h,w] (with ``use_beta``) and the binarised input ``signs`` (int8).
+    ``beta_divisor`` is "window" (beta = window sum of A / (kh*kw)) or
+    "valid" (/ the window's in-image taps).
     """
+    if beta_divisor not in ("window", "valid"):
+        raise ValueError(f"beta_divisor {beta_divisor!r}")
+    beta_mode = 0 if not use_beta else (2 if beta_divisor == "valid" else 1)
     lib = lib or load()
     x = np.ascontiguousarray(x, dtype=np.float32)
     weight_bits = np.ascontiguousarray(weight_bits, dtype=np.uint32)
@@ -171,7 +177,7 @@ def bconv(x: np.ndarray, weight_bits: np.ndarray, *, type: str, out_c: int,
     signs = np.empty((n, h, w, c), np.int8) if ("signs" in want and t != 0) else None
     a_map = np.empty((n, h, w), np.float64) if ("a_map" in want and use_beta) else None
     beta = np.empty((n, oh, ow), np.float64) if "beta" in want else None
-    rc = lib.oracle_bconv(n, h, w, c, out_c, kh, kw, sh, sw, ph, pw, phe, pwe, t, int(bool(use_beta)),
+    rc = lib.oracle_bconv(n, h, w, c, out_c, kh, kw, sh, sw, ph, pw, phe, pwe, t, beta_mode,
                           NEURON_CODES[neuron], float(scale_value), float(neuron_a), float(neuron_b),
                           _ptr(x), _ptr(weight_bits),
                           _ptr(output_scale), _ptr(output_bias), _ptr(input_scale),
@@ -192,4 +198,5 @@ def bconv_layer(layer, inputs: dict, threads: int = 0, lib=None, **kw) -> dict:
                  output_bias=inputs.get("output_bias"), input_scale=inputs.get("input_scale"),
                  input_bias=inputs.get("input_bias"), use_beta=layer.use_beta,
                  neuron=layer.neuron, scale_value=layer.scale_value, neuron_a=layer.neuron_a,
-                 neuron_b=layer.neuron_b, threads=threads, lib=lib, **kw)
+                 neuron_b=layer.neuron_b, threads=threads, lib=lib,
+                 beta_divisor="valid" if layer.beta_valid_taps else "window", **kw)

@@ -25,7 +25,9 @@
  *    before the sign and before the A map.
  *  - sign: x' < 0 -> -1 (XNOR) / 0 (AND), otherwise +1 / 1, by IEEE compare
  *    (so -0 and NaN give +1).
- *  - beta divides the window sum of A by kh*kw, out-of-image taps adding 0.
+ *  - beta divides the window sum of A by kh*kw, out-of-image taps adding 0;
+ *    the other reading of that divisor, the count of in-image taps, is
+ *    use_beta = 2.
  *  - missing output scale -> scale_value; missing biases -> 0; missing input
  *    scale -> 1.
  */
@@ -224,8 +226,9 @@ int oracle_bconv(int n, int in_h, int in_w, int in_c, int out_c, int kernel_h, i
     /* Step 4: the A map and the beta image (MPSCNNBinaryConvolution,
      * Overview, the two beta equations): A is the mean absolute value over
      * channels of the full-precision (post-affine) input; beta is the sum of A
-     * over the convolution window divided by kh*kw.  Without the flag beta is
-     * 1. */
+     * over the convolution window divided by kh*kw (use_beta 1) or, in the
+     * other reading of that divisor where the window leaves the image, by the
+     * number of in-image taps (use_beta 2).  Without the flag beta is 1. */
     for (long p = 0; p < in_pixels; ++p) {
         double sum = 0.0;
         for (int c = 0; c < in_c; ++c) sum += fabs(xd[p * in_c + c]);
@@ -237,6 +240,7 @@ int oracle_bconv(int n, int in_h, int in_w, int in_c, int out_c, int kernel_h, i
                 double b = 1.0;
                 if (use_beta) {
                     double sum = 0.0;
+                    int valid = 0;
                     for (int ky = 0; ky < kernel_h; ++ky) {
                         int iy = oy * stride_h - pad_h + ky;
                         if (iy < 0 || iy >= in_h) continue;
@@ -244,9 +248,10 @@ int oracle_bconv(int n, int in_h, int in_w, int in_c, int out_c, int kernel_h, i
                             int ix = ox * stride_w - pad_w + kx;
                             if (ix < 0 || ix >= in_w) continue;
                             sum += am[((long)i * in_h + iy) * in_w + ix];
+                            ++valid;
                         }
                     }
-                    b = sum / (double)(kernel_h * kernel_w);
+                    b = sum / (double)(use_beta == 2 ? valid : kernel_h * kernel_w);
                 }
                 bw[((long)i * out_h + oy) * out_w + ox] = b;
             }

@@ -36,8 +36,9 @@ static int out_dim(int in, int k, int s, int p, int pe)
 }
 
 /*
- * Forward pass for XNOR / AND with neuron none or ReLU.  Shapes and
- * pointers as for oracle_bconv; `out` fp32 [n][oh][ow][out_c], `acc_out`
+ * Forward pass for XNOR / AND with neuron none or ReLU.  Shapes, pointers
+ * and use_beta (0, 1: / kh*kw, 2: / in-image taps) as for oracle_bconv;
+ * `out` fp32 [n][oh][ow][out_c], `acc_out`
  * (may be NULL) int32 window sums.  Returns 0, or -1 on arguments outside
  * this baseline's scope.
  */
@@ -116,7 +117,7 @@ int packed_bconv(int n, int in_h, int in_w, int in_c, int out_c, int kh, int kw,
                         ++valid;
                     }
                 }
-                const float be = amap ? (float)(bsum / taps) : 1.0f;
+                const float be = amap ? (float)(bsum / (use_beta == 2 ? valid : taps)) : 1.0f;
                 const long o = (((long)img * oh + oy) * ow + ox) * out_c;
                 for (int co = 0; co < out_c; ++co) {
                     const uint32_t *wc = wm + (size_t)co * taps * wpt;

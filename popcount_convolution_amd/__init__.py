@@ -16,7 +16,8 @@ import numpy as np
 
 from ._binding import (  # noqa: F401  (re-exported C ABI names)
     BCONV_AND, BCONV_BINARY_WEIGHTS, BCONV_ERR_ALLOC, BCONV_ERR_HIP, BCONV_ERR_INVALID_ARGUMENT,
-    BCONV_ERR_UNSUPPORTED, BCONV_ERR_WORKSPACE, BCONV_FLAG_INT8_MFMA, BCONV_FLAG_NONE, BCONV_FLAG_USE_BETA_SCALING,
+    BCONV_ERR_UNSUPPORTED, BCONV_ERR_WORKSPACE, BCONV_FLAG_BETA_VALID_TAPS, BCONV_FLAG_INT8_MFMA, BCONV_FLAG_NONE,
+    BCONV_FLAG_USE_BETA_SCALING,
     BCONV_NEURON_NONE, BCONV_NEURON_RELU, BCONV_OK, BCONV_XNOR, NEURON_CODES, TYPE_CODES,
     BconvError, BconvLibraryMissing, bconv_create, bconv_create_fc, bconv_desc_t, bconv_destroy,
     bconv_forward, bconv_forward_accum, bconv_forward_bits, bconv_forward_bits_profiled, bconv_forward_profiled,
@@ -39,14 +40,15 @@ class BinaryConvolution:
                  weight_bits: np.ndarray, output_scale=None, output_bias=None,
                  input_scale=None, input_bias=None, use_beta: bool = False,
                  neuron: str = "none", scale_value: float = 1.0, int8_mfma: bool = False,
-                 neuron_a: float = 0.0, neuron_b: float = 0.0):
+                 neuron_a: float = 0.0, neuron_b: float = 0.0, beta_valid_taps: bool = False):
         pe = pad if pad_end is None else pad_end
         self.desc = make_desc(in_h, in_w, in_c, out_c, kernel[0], kernel[1], stride[0], stride[1],
                               pad[0], pad[1], 1, NEURON_CODES[neuron], scale_value, pe[0], pe[1],
                               neuron_a, neuron_b)
         self.type = TYPE_CODES[type]
         self.flags = (BCONV_FLAG_USE_BETA_SCALING if use_beta else BCONV_FLAG_NONE) | \
-            (BCONV_FLAG_INT8_MFMA if int8_mfma else BCONV_FLAG_NONE)
+            (BCONV_FLAG_INT8_MFMA if int8_mfma else BCONV_FLAG_NONE) | \
+            (BCONV_FLAG_BETA_VALID_TAPS if beta_valid_taps else BCONV_FLAG_NONE)
         self.handle = bconv_create(self.desc, weight_bits, output_scale, output_bias,
                                    input_scale, input_bias, self.type, self.flags)
         self.in_c, self.out_c, self.out_h, self.out_w = bconv_get_info(self.handle)
@@ -63,7 +65,7 @@ class BinaryConvolution:
                    output_bias=inputs.get("output_bias"), input_scale=inputs.get("input_scale"),
                    input_bias=inputs.get("input_bias"), use_beta=layer.use_beta,
                    neuron=layer.neuron, scale_value=layer.scale_value, int8_mfma=int8_mfma,
-                   neuron_a=layer.neuron_a, neuron_b=layer.neuron_b)
+                   neuron_a=layer.neuron_a, neuron_b=layer.neuron_b, beta_valid_taps=layer.beta_valid_taps)
 
     def workspace_bytes(self, n: int) -> int:
         return bconv_workspace_size(self.handle, n)

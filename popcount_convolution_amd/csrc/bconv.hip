@@ -71,8 +71,10 @@ bconv_status_t check_desc(const bconv_desc_t *d, int32_t type, uint32_t flags)
     if (!d) return fail(BCONV_ERR_INVALID_ARGUMENT, "desc is NULL");
     if (type != BCONV_BINARY_WEIGHTS && type != BCONV_XNOR && type != BCONV_AND)
         return fail(BCONV_ERR_INVALID_ARGUMENT, "unknown type %d", type);
-    if (flags & ~(uint32_t)(BCONV_FLAG_USE_BETA_SCALING | BCONV_FLAG_INT8_MFMA))
+    if (flags & ~(uint32_t)(BCONV_FLAG_USE_BETA_SCALING | BCONV_FLAG_INT8_MFMA | BCONV_FLAG_BETA_VALID_TAPS))
         return fail(BCONV_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", flags);
+    if ((flags & BCONV_FLAG_BETA_VALID_TAPS) && !(flags & BCONV_FLAG_USE_BETA_SCALING))
+        return fail(BCONV_ERR_INVALID_ARGUMENT, "BCONV_FLAG_BETA_VALID_TAPS requires BCONV_FLAG_USE_BETA_SCALING");
     if ((flags & BCONV_FLAG_INT8_MFMA) && type == BCONV_BINARY_WEIGHTS)
         return fail(BCONV_ERR_INVALID_ARGUMENT, "BCONV_FLAG_INT8_MFMA applies to XNOR and AND only");
     if (d->neuron < 0 || d->neuron >= BCONV_NEURON_COUNT)
@@ -269,6 +271,7 @@ bconv_status_t forward_impl(bconv_t h, void *stream, int32_t n, const float *in,
     ep.a_pad = a_map;
     ep.beta_out = beta;
     ep.neuron = bconv::Neuron{d.neuron, d.neuron_a, d.neuron_b};
+    ep.beta_valid_taps = (h->flags & BCONV_FLAG_BETA_VALID_TAPS) ? 1 : 0;
     if (sink == Sink::Bits) {
         ep.bits_out = static_cast<uint32_t *>(dst);
         ep.out_words = out_words;

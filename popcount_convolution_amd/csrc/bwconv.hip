@@ -23,6 +23,7 @@ struct BwArgs {
     const float *scale, *bias;
     const float *a_pad;  // zero-halo A map or nullptr (beta = 1)
     float *beta_out;
+    int beta_valid;      // beta divisor: in-image taps instead of kh*kw
     int rows, cols;
     float scale_value;
     Neuron neuron;
@@ -97,12 +98,12 @@ __global__ __launch_bounds__(256) void bwconv_kernel(BwArgs a)
     if (!live) return;
     float be = 1.0f;
     if (a.a_pad) {
-        // beta: window sum of the zero-halo A map / (kh*kw)
+        // beta: window sum of the zero-halo A map / (kh*kw, or the in-image taps)
         const float *ap = a.a_pad + (img * a.rows + (long long)oy * a.sh) * a.cols + (long long)ox * a.sw;
         float sum = 0.0f;
         for (int ky = 0; ky < a.kh; ++ky)
             for (int kx = 0; kx < a.kw; ++kx) sum += ap[ky * a.cols + kx];
-        be = sum / (float)(a.kh * a.kw);
+        be = sum / (float)(a.beta_valid ? window_valid_taps(oy, ox, a.sh, a.sw, a.ph, a.pw, a.kh, a.kw, a.in_h, a.in_w) : a.kh * a.kw);
         if (cb == 0) a.beta_out[m] = be;
     }
     if (a.bits_out) {
@@ -160,6 +161,7 @@ hipError_t launch_bwconv(const Geom &g, const Launch &L, const float *x, const f
     a.scale = e.scale;
     a.bias = e.bias;
     a.a_pad = e.a_pad;
+    a.beta_valid = e.beta_valid_taps;
     a.beta_out = e.beta_out;
     a.rows = g.bits_rows;
     a.cols = g.bits_cols;

@@ -71,6 +71,7 @@ struct MmaArgs {
     const float *scale, *bias;
     const float *a_pad;  // zero-halo A map or nullptr (beta = 1)
     float *beta_out;
+    int beta_valid;      // beta divisor: in-image taps instead of kh*kw
     float scale_value;
     Neuron neuron;
     float *out;
@@ -281,14 +282,15 @@ __global__ __launch_bounds__(kThreads) void bwmma_kernel(MmaArgs a)
             sc[u][r] = a.scale ? a.scale[c] : a.scale_value;
             bi[u][r] = a.bias ? a.bias[c] : 0.0f;
         }
-    // beta of this lane's pixel: window sum of the zero-halo A map / (kh*kw)
+    // beta of this lane's pixel: window sum of the zero-halo A map / (kh*kw,
+    // or the in-image taps)
     float be = 1.0f;
     if (a.a_pad) {
         const float *ap = a.a_pad + ((long long)img * a.rows + oy * a.sh) * a.cols + ox * a.sw;
         float sum = 0.0f;
         for (int ky = 0; ky < a.kh; ++ky)
             for (int kx = 0; kx < a.kw; ++kx) sum += ap[ky * a.cols + kx];
-        be = sum / (float)(a.kh * a.kw);
+        be = sum / (float)(a.beta_valid ? window_valid_taps(oy, ox, a.sh, a.sw, a.ph, a.pw, a.kh, a.kw, a.in_h, a.in_w) : a.kh * a.kw);
     }
 
     const u32x4 *gfrag = a.frag + (long long)ntile * a.ksteps * kStepU4;
@@ -458,6 +460,7 @@ hipError_t launch_bwmma(const Geom &g, const Launch &L, const float *x, const fl
     a.scale = e.scale;
     a.bias = e.bias;
     a.a_pad = e.a_pad;
+    a.beta_valid = e.beta_valid_taps;
     a.beta_out = e.beta_out;
     a.scale_value = e.scale_value;
     a.neuron = e.neuron;

@@ -158,6 +158,7 @@ struct I8Args {
     const float *scale, *bias;
     const float *a_pad;
     float *beta_out;
+    int beta_valid;  // beta divisor: in-image taps instead of kh*kw
     float scale_value;
     Neuron neuron;
     float *out;
@@ -165,6 +166,7 @@ struct I8Args {
     uint32_t *bits_out;  // packed sign bits instead of out (see Epilogue)
     int out_words;
     int n, out_c, out_h, out_w, kh, kw, sh, sw, rows, cols, cpad;
+    int in_h, in_w, ph, pw;
     int chunks, ksteps, ntiles, mtiles, m_total;
     int act_bytes, out_bytes, vec_out;
     int weights_major;  // consecutive tiles share a weight tile (weights outweigh activations)
@@ -225,7 +227,7 @@ __global__ __launch_bounds__(kThreads) void i8mma_kernel(I8Args a)
         float sum = 0.0f;
         for (int ky = 0; ky < a.kh; ++ky)
             for (int kx = 0; kx < a.kw; ++kx) sum += ap[ky * a.cols + kx];
-        be = sum / (float)(a.kh * a.kw);
+        be = sum / (float)(a.beta_valid ? window_valid_taps(oy, ox, a.sh, a.sw, a.ph, a.pw, a.kh, a.kw, a.in_h, a.in_w) : a.kh * a.kw);
     }
 
     i32x4 acc[4];
@@ -404,6 +406,7 @@ hipError_t launch_i8mma(const Geom &g, const Launch &L, const int8_t *act, const
     a.scale = e.scale;
     a.bias = e.bias;
     a.a_pad = e.a_pad;
+    a.beta_valid = e.beta_valid_taps;
     a.beta_out = e.beta_out;
     a.scale_value = e.scale_value;
     a.neuron = e.neuron;
@@ -419,6 +422,10 @@ hipError_t launch_i8mma(const Geom &g, const Launch &L, const int8_t *act, const
     a.kw = g.kw;
     a.sh = g.sh;
     a.sw = g.sw;
+    a.in_h = g.in_h;
+    a.in_w = g.in_w;
+    a.ph = g.ph;
+    a.pw = g.pw;
     a.rows = g.bits_rows;
     a.cols = g.bits_cols;
     a.cpad = i8_cpad(g.in_c);

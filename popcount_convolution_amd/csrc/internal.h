@@ -174,7 +174,21 @@ struct Epilogue {
     // for the value y the fp32 output would hold, bits past out_c zero.
     uint32_t *bits_out;
     int out_words;
+    // beta divides by the window's in-image tap count instead of kh*kw
+    int beta_valid_taps;
 };
+
+// Number of taps of output pixel (oy, ox)'s window that lie inside the image
+// (at least 1: every window holds an in-image tap since pads < kernel).
+__device__ __forceinline__ int window_valid_taps(int oy, int ox, int sh, int sw, int ph, int pw, int kh, int kw,
+                                                 int in_h, int in_w)
+{
+    const int iy0 = oy * sh - ph, ix0 = ox * sw - pw;
+    const int r0 = iy0 < 0 ? -iy0 : 0, r1 = in_h - iy0 < kh ? in_h - iy0 : kh;
+    const int c0 = ix0 < 0 ? -ix0 : 0, c1 = in_w - ix0 < kw ? in_w - ix0 : kw;
+    const int v = (r1 - r0) * (c1 - c0);
+    return v > 0 ? v : 1;
+}
 
 // Launchers (each returns the hipGetLastError() of its launch).
 hipError_t launch_pack(const Geom &g, hipStream_t s, const float *x, const float *in_scale,

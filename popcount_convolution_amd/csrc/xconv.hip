@@ -83,7 +83,7 @@ __global__ __launch_bounds__(256) void xconv_generic(XArgs a, int and_mode)
         float sum = 0.0f;
         for (int ky = 0; ky < a.kh; ++ky)
             for (int kx = 0; kx < a.kw; ++kx) sum += ap[ky * a.cols + kx];
-        be = sum / (float)(a.kh * a.kw);
+        be = sum / (float)(a.beta_valid ? window_valid_taps(oy, ox, a.sh, a.sw, a.ph, a.pw, a.kh, a.kw, a.in_h, a.in_w) : a.kh * a.kw);
         if (tile == 0 && lane == 0) a.beta_out[pix] = be;
     }
     if (a.bits_out)
@@ -133,6 +133,7 @@ XArgs make_args(const Geom &g, const uint32_t *bits, const LaneWeights &w, const
     a.scale = e.scale;
     a.bias = e.bias;
     a.a_pad = e.a_pad;
+    a.beta_valid = e.beta_valid_taps;
     a.beta_out = e.beta_out;
     a.scale_value = e.scale_value;
     a.neuron = e.neuron;

@@ -34,6 +34,7 @@ struct XArgs {
     const float *scale, *bias;
     const float *a_pad;  // zero-halo A map or nullptr (beta = 1)
     float *beta_out;
+    int beta_valid;      // beta divisor: in-image taps instead of kh*kw
     float scale_value;
     Neuron neuron;
     float *out;
@@ -145,7 +146,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void x
 #pragma unroll
             for (int r = 0; r < KH; ++r)
                 colsum += __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ar, coff, abase + r * a.cols * 4, 0));
-            be_lane = add_row_shifted<KW>(colsum, colsum) * (1.0f / (float)(KH * KW));
+            be_lane = add_row_shifted<KW>(colsum, colsum);
         } else if constexpr (KH <= 4 && NCOL <= 16) {
             // One load brings the strip's KH x NCOL patch (row r in lanes
             // 16r..16r+15); cross-lane sums then add each window.
@@ -162,7 +163,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void x
             float sum = 0.0f;
 #pragma unroll
             for (int kx = 0; kx < KW; ++kx) sum += __shfl(colsum, (lane * SW + kx) & 63);
-            be_lane = sum * (1.0f / (float)(KH * KW));
+            be_lane = sum;
         } else {
             float sum = 0.0f;
             if (lane < P && ow0 + lane < a.out_w) {
@@ -173,8 +174,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void x
                         sum += __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                                              ar, (uint32_t)(lane * SW * 4), abase + (ky * a.cols + kx) * 4, 0));
             }
-            be_lane = sum * (1.0f / (float)(KH * KW));
+            be_lane = sum;
         }
+        // window sum / (kh*kw), or / the in-image taps of the lane's pixel
+        if (a.beta_valid)
+            be_lane = be_lane / (float)window_valid_taps(oy, ow0 + lane, a.sh, SW, a.ph, a.pw, KH, KW, a.in_h, a.in_w);
+        else
+            be_lane = be_lane * (1.0f / (float)(KH * KW));
     }
 
     // Epilogue operands are loaded here, so their latency overlaps the first

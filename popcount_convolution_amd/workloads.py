@@ -61,6 +61,8 @@ class Layer:
     # activation parameters (see the neuron list of the C header)
     neuron_a: float = 0.0
     neuron_b: float = 0.0
+    # beta divides by the window's in-image taps instead of kh*kw
+    beta_valid_taps: bool = False
 
     @property
     def pad_h_end(self) -> int:

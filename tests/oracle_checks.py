@@ -330,6 +330,47 @@ def check_beta_constant_input(lib):
     np.testing.assert_allclose(rfc["beta"], v, rtol=1e-15)
 
 
+def check_beta_valid_taps(lib):
+    """The valid-tap reading of beta's divisor (the other reading of the first
+    beta equation where the window leaves the image): a mean of A over the
+    window's in-image taps.
+    - constant post-affine input v: beta = |v| at every position, corners and
+      edges included, for odd and even kernels, strides 1 and 2;
+    - a 1 x 2 image whose pixels have A = 1 and 3 under a 3x3 window, pad 1:
+      both windows see both pixels, so beta = (1 + 3) / 2 = 2 (the kh*kw
+      divisor gives 4/9); a single-pixel image gives beta = A of that pixel;
+    - windows inside the image read the same beta under both divisors."""
+    c = 37
+    isc, ib = np.full(c, 2.0, np.float32), np.full(c, -3.0, np.float32)
+    v = abs(0.25 * 2.0 - 3.0)
+    for (h, w), k, st, p, pe in [((6, 7), 3, 1, 1, 1), ((6, 7), 4, 1, 2, 1), ((7, 9), 2, 2, 1, 0),
+                                 ((9, 8), 5, 2, 2, 2), ((5, 5), 1, 1, 0, 0)]:
+        x = np.full((2, h, w, c), 0.25, np.float32)
+        wb = _rand_bits(_rng(41), (3, k, k, 2))
+        r = _run(lib, x, wb, "xnor", 3, k=(k, k), s=(st, st), p=(p, p), pad_end=(pe, pe), use_beta=True,
+                 beta_divisor="valid", input_scale=isc, input_bias=ib)
+        np.testing.assert_allclose(r["beta"], v, rtol=1e-15, err_msg=f"k{k} s{st} pad {p}/{pe}")
+    x = np.empty((1, 1, 2, 4), np.float32)
+    x[0, 0, 0] = [1.0, -1.0, 1.0, -1.0]   # A = 1
+    x[0, 0, 1] = [3.0, -3.0, -3.0, 3.0]   # A = 3
+    wb = _rand_bits(_rng(42), (2, 3, 3, 1))
+    r = _run(lib, x, wb, "and", 2, k=(3, 3), p=(1, 1), use_beta=True, beta_divisor="valid")
+    np.testing.assert_allclose(r["beta"][0, 0], [2.0, 2.0], rtol=1e-15)
+    r9 = _run(lib, x, wb, "and", 2, k=(3, 3), p=(1, 1), use_beta=True)
+    np.testing.assert_allclose(r9["beta"][0, 0], [4.0 / 9.0, 4.0 / 9.0], rtol=1e-15)
+    r1 = _run(lib, x[:, :, :1], wb, "binary_weights", 2, k=(3, 3), p=(1, 1), use_beta=True,
+              beta_divisor="valid")
+    np.testing.assert_allclose(r1["beta"][0, 0, 0], 1.0, rtol=1e-15)
+    rng = _rng(43)
+    x = rng.normal(size=(2, 6, 8, 33)).astype(np.float32)
+    wb = _rand_bits(rng, (4, 3, 3, 2))
+    rv = _run(lib, x, wb, "xnor", 4, k=(3, 3), p=(1, 1), use_beta=True, beta_divisor="valid")
+    rw = _run(lib, x, wb, "xnor", 4, k=(3, 3), p=(1, 1), use_beta=True)
+    np.testing.assert_array_equal(rv["beta"][:, 1:-1, 1:-1], rw["beta"][:, 1:-1, 1:-1])
+    np.testing.assert_array_equal(rv["acc"], rw["acc"])
+    assert not np.array_equal(rv["beta"], rw["beta"])
+
+
 def check_a_map_definition(lib):
     """A is the mean over channels of |x'| (Nc = Cin, not the padded word
     width), checked with float64 numpy on a random input and affine."""
@@ -537,4 +578,5 @@ ALL_CHECKS = [
     check_a_map_definition, check_epilogue_closed_form, check_sign_under_affine,
     check_tail_bits_ignored, check_degenerate_single_channel,
     check_accumulator_parity_and_range, check_neuron_closed_forms, check_neuron_identities,
+    check_beta_valid_taps,
 ]

@@ -127,6 +127,41 @@ def test_sweep(dev, layer):
     parity.compare(layer, inputs, gen, ref=ref)
 
 
+# ------------------------------------------------------- valid-tap beta
+
+_VT = workloads.BENCH_LAYER.with_(n=2, in_h=13, in_w=17, beta_valid_taps=True)
+VALID_TAP_CASES = [
+    (_VT.with_(name="vt_xnor_k3"), False, False),
+    (_VT.with_(name="vt_xnor_k3_generic"), True, False),
+    (_VT.with_(name="vt_xnor_k3_int8"), False, True),
+    (_VT.with_(name="vt_and_k4_centred", type="and", kernel_h=4, kernel_w=4, pad_h=2, pad_w=2, pad_bottom=1,
+               pad_right=1), False, False),
+    (_VT.with_(name="vt_xnor_k5_s2", kernel_h=5, kernel_w=5, pad_h=2, pad_w=2, stride_h=2, stride_w=2), False, False),
+    (_VT.with_(name="vt_xnor_k2_s2_centred", kernel_h=2, kernel_w=2, pad_h=1, pad_w=1, pad_bottom=0, pad_right=0,
+               stride_h=2, stride_w=2, in_c=64), False, False),
+    (_VT.with_(name="vt_binary_weights", type="binary_weights", in_c=64), False, False),
+    (_VT.with_(name="vt_binary_weights_generic", type="binary_weights", in_c=40, stride_h=2, stride_w=2), True, False),
+    (_VT.with_(name="vt_fc", n=3, in_h=4, in_w=5, in_c=96, out_c=70, kernel_h=4, kernel_w=5, pad_h=0, pad_w=0),
+     False, False),
+]
+
+
+@pytest.mark.parametrize("layer,generic,int8", VALID_TAP_CASES, ids=[c[0].name for c in VALID_TAP_CASES])
+def test_beta_valid_taps(dev, layer, generic, int8):
+    """BCONV_FLAG_BETA_VALID_TAPS on every kernel path: beta (from the
+    workspace), window sums and outputs against the oracle's valid-tap
+    reading; the FC shape has no padding, so the flag changes nothing."""
+    inputs = workloads.make_inputs(layer, 3100 + VALID_TAP_CASES.index((layer, generic, int8)))
+    _log(f"valid taps {layer.name} generic={generic} int8={int8}")
+    got = parity.run_gpu(layer, inputs, dev, generic=generic, int8_mfma=int8)
+    ref = parity.compare(layer, inputs, got)
+    window = oracle.bconv_layer(layer.with_(beta_valid_taps=False), inputs)
+    if layer.pad_h or layer.pad_w:
+        assert not np.allclose(ref["beta"], window["beta"])
+    else:
+        np.testing.assert_array_equal(ref["beta"], window["beta"])
+
+
 # ------------------------------------------------------- specialised kernels
 
 # (kernel_h, kernel_w, words per pixel, stride) of every compiled instance of

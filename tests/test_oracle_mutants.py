@@ -27,12 +27,13 @@ MUTANTS = {
                         "if (ix < 0 || ix >= in_w) ix = ix < 0 ? 0 : in_w - 1;")],
     "padding_row_clamps": [("if (iy < 0 || iy >= in_h) continue; /* padded tap: nothing */",
                             "if (iy < 0 || iy >= in_h) iy = iy < 0 ? 0 : in_h - 1;")],
-    "beta_divides_by_valid_taps": [
-        ("double sum = 0.0;\n                    for (int ky",
-         "double sum = 0.0; int cnt = 0;\n                    for (int ky"),
-        ("sum += am[((long)i * in_h + iy) * in_w + ix];",
-         "sum += am[((long)i * in_h + iy) * in_w + ix]; ++cnt;"),
-        ("b = sum / (double)(kernel_h * kernel_w);", "b = sum / (double)cnt;")],
+    "beta_divides_by_valid_taps": [("b = sum / (double)(use_beta == 2 ? valid : kernel_h * kernel_w);",
+                                    "b = sum / (double)valid;")],
+    "valid_tap_beta_divides_by_window": [("b = sum / (double)(use_beta == 2 ? valid : kernel_h * kernel_w);",
+                                          "b = sum / (double)(kernel_h * kernel_w);")],
+    "valid_tap_count_includes_padding": [("                            ++valid;\n", ""),
+                                         ("                    int valid = 0;\n",
+                                          "                    int valid = kernel_h * kernel_w;\n")],
     "affine_offset_then_scale": [("v = fmaf(v, s, b);", "v = (v + b) * s;")],
     "affine_two_roundings": [("v = fmaf(v, s, b);", "v = (float)(v * s) + b;")],
     "a_map_over_word_width": [("am[p] = sum / (double)in_c;", "am[p] = sum / (double)(words * 32);")],

@@ -18,6 +18,8 @@ CASES = [
     BASE.with_(name="packed_xnor_k4_centred", kernel_h=4, kernel_w=4, pad_h=2, pad_w=2, pad_bottom=1, pad_right=1,
                in_c=33),
     BASE.with_(name="packed_fc", n=3, in_h=4, in_w=5, in_c=40, out_c=12, kernel_h=4, kernel_w=5, pad_h=0, pad_w=0),
+    BASE.with_(name="packed_and_beta_valid_taps", type="and", use_beta=True, beta_valid_taps=True, kernel_h=4,
+               kernel_w=4, pad_h=2, pad_w=2, pad_bottom=1, pad_right=1, neuron="relu"),
     workloads.LAYERS[0],
 ]
 
