@@ -492,8 +492,9 @@ hipError_t launch_bwmma(const Geom &g, const Launch &L, const float *x, const fl
     const long long out_bytes = m_total * g.out_c * 4;
     if (m_total == 0) return hipSuccess;
     // every buffer offset and work index stays below 2^31
+    // (the fragment table itself may exceed 2 GiB: it is indexed with 64-bit offsets)
     if (x_bytes >= 0x7fffffffLL || out_bytes >= 0x7fffffffLL || mtiles * a.ntiles >= 0x7fffffffLL - kXcds ||
-        (long long)a.ksteps * kStepU4 * 16 >= 0x7fffffffLL)
+        (long long)a.ksteps * kStepU4 >= 0x7fffffffLL)
         return hipErrorInvalidValue;
     a.m_total = (int)m_total;
     a.mtiles = (int)mtiles;

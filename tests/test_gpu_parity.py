@@ -535,6 +535,48 @@ def test_two_streams_share_a_handle(dev):
         conv.close()
 
 
+# ------------------------------------------------------------ maximum sizes
+
+MAX_CHANNELS = 1 << 20   # the C ABI's in_c limit
+MAX_EXTENT = 1 << 16     # the C ABI's image extent limit
+MAX_CASES = [
+    # in_c * kh * kw = 2^24, the largest window the C ABI accepts: FC shape
+    # (matrix route) and a conv shape with four outputs (shape-generic kernel)
+    workloads.Layer("max_window_fc_xnor", "xnor", 1, 4, 4, MAX_CHANNELS, 3, 4, 4),
+    workloads.Layer("max_window_fc_and", "and", 1, 4, 4, MAX_CHANNELS, 3, 4, 4, use_beta=True),
+    workloads.Layer("max_window_fc_binary_weights", "binary_weights", 1, 4, 4, MAX_CHANNELS, 3, 4, 4),
+    workloads.Layer("max_window_conv_xnor", "xnor", 1, 5, 5, MAX_CHANNELS, 2, 4, 4, use_beta=True),
+    # the largest image extent, in either direction
+    workloads.Layer("max_width", "xnor", 1, 1, MAX_EXTENT, 32, 70, 3, 3, 1, 1, 1, 1, use_beta=True),
+    workloads.Layer("max_height_and", "and", 1, MAX_EXTENT, 1, 40, 5, 3, 3, 2, 1, 1, 1),
+]
+
+
+@pytest.mark.parametrize("layer", MAX_CASES, ids=[l.name for l in MAX_CASES])
+def test_maximum_sizes(dev, layer):
+    """The C ABI's largest window (2^24 bits: window sums exact in int32 and
+    fp32) and largest image extents, against the oracle."""
+    inputs = workloads.make_inputs(layer, 4400 + MAX_CASES.index(layer))
+    _log(f"max {layer.name}")
+    got = parity.run_gpu(layer, inputs, dev)
+    parity.compare(layer, inputs, got)
+
+
+def test_maximum_window_is_exact(dev):
+    """All 2^24 products of the largest window agree: the XNOR and AND sums
+    reach exactly 2^24 (the top of the exact fp32 integers) and the output is
+    2^24 * scale."""
+    for form in ("xnor", "and"):
+        layer = workloads.Layer("max_window_ones", form, 1, 4, 4, MAX_CHANNELS, 2, 4, 4,
+                                oscale_dist=None, obias_dist=None, scale_value=0.5)
+        inputs = workloads.make_inputs(layer, 1)
+        inputs["x"] = np.abs(inputs["x"]) + 0.5
+        inputs["weight_bits"][:] = 0xFFFFFFFF
+        got = parity.run_gpu(layer, inputs, dev)
+        assert np.all(got["acc"] == (1 << 24)), form
+        assert np.all(got["out"] == np.float32(1 << 23)), form
+
+
 def test_argument_errors(dev):
     layer = workloads.BENCH_LAYER.with_(n=2)
     inputs = workloads.make_inputs(layer, 5)
