@@ -62,6 +62,10 @@ constexpr int kStage = 18;      // K steps of weight fragments per LDS stage
 constexpr int kStepU4 = 256;    // 16-byte fragment entries per K step (4 blocks x 64 lanes)
 constexpr int kXcds = 8;
 constexpr int kThreads = 512;   // 8 waves: 4 pixel groups x 2 K halves
+#ifndef BWMMA_PREFETCH
+#define BWMMA_PREFETCH 2
+#endif
+constexpr int kPrefetch = BWMMA_PREFETCH;  // K steps of input loads in flight per wave
 constexpr int kRedBytes = 4 * 4 * 64 * 16;  // LDS for summing the K halves
 constexpr uint32_t kOob = 0x80000000u;  // buffer offset past any range: loads return 0
 
@@ -298,29 +302,33 @@ __global__ __launch_bounds__(kThreads) void bwmma_kernel(MmaArgs a)
         const int cnt = a.ksteps - s0 < kStage ? a.ksteps - s0 : kStage;
         const int half = (cnt + 1) >> 1;
         const int sb = s0 + (khalf ? half : 0), se = s0 + (khalf ? cnt : half);
-        // Two input buffers, each refilled right after its step is split:
-        // a load has two steps of work to arrive, and the matrix-core work
-        // of one step overlaps the split of the next.  Loads past this
-        // wave's last step read in-bounds data (or zero) that is never used.
+        // A ring of kPrefetch input buffers, each refilled right after its
+        // step is split: a load has kPrefetch steps of work to arrive, and
+        // the matrix-core work of one step overlaps the split of the next.
+        // Loads past this wave's last step read in-bounds data (or zero) that
+        // is never used.
         StepPos lpos = step_pos(a, sb);
-        float xa[8], xb[8];
-        load_step<VEC8, AFFINE>(a, xr, lpos, lane_base, iy0, ix0, cg, live, xa);
-        advance(a, lpos);
-        load_step<VEC8, AFFINE>(a, xr, lpos, lane_base, iy0, ix0, cg, live, xb);
-        advance(a, lpos);
+        float xbuf[kPrefetch][8];
+#pragma unroll
+        for (int i = 0; i < kPrefetch; ++i) {
+            load_step<VEC8, AFFINE>(a, xr, lpos, lane_base, iy0, ix0, cg, live, xbuf[i]);
+            advance(a, lpos);
+        }
         __syncthreads();  // previous stage fully read
         for (int i = threadIdx.x; i < cnt * kStepU4; i += kThreads) stage[i] = gfrag[(long long)s0 * kStepU4 + i];
         __syncthreads();
         int s = sb;
-        for (; s + 1 < se; s += 2) {
-            mma_step(acc, xa, stage + (s - s0) * kStepU4 + lane);
-            load_step<VEC8, AFFINE>(a, xr, lpos, lane_base, iy0, ix0, cg, live, xa);
-            advance(a, lpos);
-            mma_step(acc, xb, stage + (s + 1 - s0) * kStepU4 + lane);
-            load_step<VEC8, AFFINE>(a, xr, lpos, lane_base, iy0, ix0, cg, live, xb);
-            advance(a, lpos);
+        for (; s + kPrefetch <= se; s += kPrefetch) {
+#pragma unroll
+            for (int i = 0; i < kPrefetch; ++i) {
+                mma_step(acc, xbuf[i], stage + (s + i - s0) * kStepU4 + lane);
+                load_step<VEC8, AFFINE>(a, xr, lpos, lane_base, iy0, ix0, cg, live, xbuf[i]);
+                advance(a, lpos);
+            }
         }
-        if (s < se) mma_step(acc, xa, stage + (s - s0) * kStepU4 + lane);
+#pragma unroll
+        for (int i = 0; i < kPrefetch - 1; ++i)
+            if (s + i < se) mma_step(acc, xbuf[i], stage + (s + i - s0) * kStepU4 + lane);
     }
 
     // Sum the two K halves: the first half keeps channel blocks 0,1, the
@@ -372,7 +380,18 @@ __global__ __launch_bounds__(kThreads) void bwmma_kernel(MmaArgs a)
     for (int u = 0; u < 2; ++u) {
         const int co = ntile * kChanTile + 16 * (keep + u) + 4 * (lane >> 4);
         f32x4 v = res[u];
-        if (!a.acc_out) {
+        // one loop per output form, so no per-element select among activations
+        if (a.acc_out) {
+        } else if (a.neuron.type == kNeuronNone) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = __builtin_fmaf(v[r] * sc[u][r], be, bi[u][r]);
+        } else if (a.neuron.type == kNeuronRelu) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float y = __builtin_fmaf(v[r] * sc[u][r], be, bi[u][r]);
+                v[r] = (y < 0.0f) ? 0.0f : y;
+            }
+        } else {
 #pragma unroll
             for (int r = 0; r < 4; ++r) v[r] = epilogue_value(v[r], sc[u][r], be, bi[u][r], a.neuron);
         }
