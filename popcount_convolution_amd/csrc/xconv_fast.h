@@ -21,6 +21,8 @@
 
 #include "internal.h"
 
+#include <type_traits>
+
 namespace bconv {
 
 
@@ -198,9 +200,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void x
     // set weight bit as a disagreement; those bits are total - (in-image
     // rectangle), from the lane's prefix sums rect[a][b] (taps ky < a, kx < b).
     // A strip needs rows r0 and r1 of the table and the total.
-    int rt0[KW + 1], rt1[KW + 1], rtotal = 0;
-#pragma unroll
-    for (int c = 0; c <= KW; ++c) rt0[c] = rt1[c] = 0;
+    // (read only on border strips, where they are loaded below)
+    int rt0[KW + 1], rt1[KW + 1], rtotal;
     const int ixa = ow0 * SW - a.pw;                 // first pixel's first tap column
     const int ixz = (ow0 + P - 1) * SW - a.pw + KW;  // one past the last pixel's last tap
     const bool border = r0 > 0 || r1 < KH || ixa < 0 || ixz > a.in_w;
@@ -280,64 +281,81 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void x
         __builtin_amdgcn_readfirstlane((uint32_t)(((img * a.out_h + oy) * a.out_w + ow0) * a.out_c) * 4u);
     const uint32_t ostep = (uint32_t)a.out_c * 4u;
     // the output value's integer part: window sum (XNOR with its border correction)
-    auto window_value = [&](int p, int ox) -> int {
-        if (AND) return (int)acc[p];  // a zero word at a padded tap adds nothing
-        const int ix0 = ox * SW - a.pw;
-        const int c0 = ix0 < 0 ? -ix0 : 0;
-        const int c1 = a.in_w - ix0 < KW ? a.in_w - ix0 : KW;
-        const int valid = (r1 - r0) * (c1 - c0);
-        int corr = 0;
-        if (valid != KH * KW) {
-            // set weight bits at padded taps = total - in-image rectangle
-            // (c0, c1 are wave-uniform: a select chain, no register indexing)
-            int a0 = 0, a1 = 0, b0 = 0, b1 = 0;
+    const int full_taps = a.in_c * (KH * KW);  // XNOR value's constant when every tap is in the image
+    // The output value's integer part: the window sum (XNOR with its border
+    // correction).  FULL: every tap of every pixel of the strip is in the
+    // image, so no border term (decided once per wave, not per pixel).
+    auto window_value = [&](auto full, int p, int ox) -> int {
+        if constexpr (AND) {
+            return (int)acc[p];  // a zero word at a padded tap adds nothing
+        } else if constexpr (decltype(full)::value) {
+            return full_taps - 2 * (int)acc[p];
+        } else {
+            const int ix0 = ox * SW - a.pw;
+            const int c0 = ix0 < 0 ? -ix0 : 0;
+            const int c1 = a.in_w - ix0 < KW ? a.in_w - ix0 : KW;
+            const int valid = (r1 - r0) * (c1 - c0);
+            int corr = 0;
+            if (valid != KH * KW) {
+                // set weight bits at padded taps = total - in-image rectangle
+                // (c0, c1 are wave-uniform: a select chain, no register indexing)
+                int a0 = 0, a1 = 0, b0 = 0, b1 = 0;
 #pragma unroll
-            for (int c = 0; c <= KW; ++c) {
-                if (c == c0) { a0 = rt0[c]; a1 = rt1[c]; }
-                if (c == c1) { b0 = rt0[c]; b1 = rt1[c]; }
+                for (int c = 0; c <= KW; ++c) {
+                    if (c == c0) { a0 = rt0[c]; a1 = rt1[c]; }
+                    if (c == c1) { b0 = rt0[c]; b1 = rt1[c]; }
+                }
+                corr = rtotal - (b1 - b0 - a1 + a0);
             }
-            corr = rtotal - (b1 - b0 - a1 + a0);
+            return a.in_c * valid - 2 * ((int)acc[p] - corr);
         }
-        return a.in_c * valid - 2 * ((int)acc[p] - corr);
     };
-    if (a.bits_out) {
-#pragma unroll
-        for (int p = 0; p < P; ++p) {
-            const int ox = ow0 + p;
-            if (ox >= a.out_w) break;
-            const float be = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(be_lane), p));
-            store_tile_bits(a.bits_out, ((long long)img * a.out_h + oy) * a.out_w + ox, a.out_words, (int)tile,
-                            co_ok && sign_bit(epilogue_value((float)window_value(p, ox), sc, be, bi, a.neuron)));
-        }
-        return;
-    }
-    // One unrolled loop per output form (window sums, values with and without
-    // ReLU), so no per-pixel select between them.  Lanes past out_c store at an
-    // out-of-range offset, which the buffer range check discards.
+    // Lanes past out_c store at an out-of-range offset, which the buffer range
+    // check discards.
     const uint32_t coff = co_ok ? (uint32_t)(co * 4) : 0x80000000u;
-    auto store_all = [&](auto value_bits) {
+    auto emit = [&](auto full) {
+        if (a.bits_out) {
 #pragma unroll
-        for (int p = 0; p < P; ++p) {
-            const int ox = ow0 + p;
-            if (ox >= a.out_w) break;
-            const float be = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(be_lane), p));
-            __builtin_amdgcn_raw_buffer_store_b32(value_bits(window_value(p, ox), be), orr, coff,
-                                                  __builtin_amdgcn_readfirstlane(obase + (uint32_t)p * ostep), kStoreSc1);
+            for (int p = 0; p < P; ++p) {
+                const int ox = ow0 + p;
+                if (ox >= a.out_w) break;
+                const float be = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(be_lane), p));
+                store_tile_bits(a.bits_out, ((long long)img * a.out_h + oy) * a.out_w + ox, a.out_words, (int)tile,
+                                co_ok && sign_bit(epilogue_value((float)window_value(full, p, ox), sc, be, bi, a.neuron)));
+            }
+            return;
         }
+        // One unrolled loop per output form (window sums, values with and
+        // without ReLU), so no per-pixel select between them.
+        auto store_all = [&](auto value_bits) {
+#pragma unroll
+            for (int p = 0; p < P; ++p) {
+                const int ox = ow0 + p;
+                if (ox >= a.out_w) break;
+                const float be = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(be_lane), p));
+                __builtin_amdgcn_raw_buffer_store_b32(value_bits(window_value(full, p, ox), be), orr, coff,
+                                                      __builtin_amdgcn_readfirstlane(obase + (uint32_t)p * ostep),
+                                                      kStoreSc1);
+            }
+        };
+        if (a.acc_out)
+            store_all([](int v, float) { return (uint32_t)v; });
+        else if (a.neuron.type == kNeuronRelu)
+            store_all([&](int v, float be) {
+                const float r = __builtin_fmaf((float)v * sc, be, bi);
+                return __builtin_bit_cast(uint32_t, (r < 0.0f) ? 0.0f : r);
+            });
+        else if (a.neuron.type == kNeuronNone)
+            store_all([&](int v, float be) { return __builtin_bit_cast(uint32_t, __builtin_fmaf((float)v * sc, be, bi)); });
+        else
+            store_all([&](int v, float be) {
+                return __builtin_bit_cast(uint32_t, epilogue_value((float)v, sc, be, bi, a.neuron));
+            });
     };
-    if (a.acc_out)
-        store_all([](int v, float) { return (uint32_t)v; });
-    else if (a.neuron.type == kNeuronRelu)
-        store_all([&](int v, float be) {
-            const float r = __builtin_fmaf((float)v * sc, be, bi);
-            return __builtin_bit_cast(uint32_t, (r < 0.0f) ? 0.0f : r);
-        });
-    else if (a.neuron.type == kNeuronNone)
-        store_all([&](int v, float be) { return __builtin_bit_cast(uint32_t, __builtin_fmaf((float)v * sc, be, bi)); });
+    if (!AND && border)
+        emit(std::false_type{});
     else
-        store_all([&](int v, float be) {
-            return __builtin_bit_cast(uint32_t, epilogue_value((float)v, sc, be, bi, a.neuron));
-        });
+        emit(std::true_type{});
 }
 
 template <int KH, int KW, int CW, int SW, int P>
