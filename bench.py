@@ -16,6 +16,10 @@ HBM.  Prints one JSON line:
              roofline against the dense int8 MFMA peak or HBM; and the layer
              with its output written as packed sign bits for a next binary
              layer (bconv_forward_bits), timed the same way;
+  calibration   measured ceilings of this GPU: the popcount path's two
+             instructions on registers (the library's calibration kernel, T
+             bit-MAC/s; the roofline object adds the kernel's fraction of it
+             beside the published peak) and a 1 GiB device copy (GB/s);
   cpu_baseline  the CPU oracle timed on a bounded sample of the same layer;
   cpu_packed_baseline  (XNOR / AND) the packed-bit popcount form on the CPU
              (the oracle package's second reference point), whole batch.
@@ -100,6 +104,8 @@ def parse():
                    help="time the convolution over a sweep of strides, paddings and kernel sizes")
     p.add_argument("--sweep-widths", action="store_true",
                    help="with --sweep: also time every strip width of the specialised convolution")
+    p.add_argument("--no-calibration", action="store_true",
+                   help="skip the measured popcount-peak and HBM-copy calibration")
     p.add_argument("--no-bits", action="store_true",
                    help="skip the packed sign-bit output comparison")
     p.add_argument("--profile-only", action="store_true",
@@ -326,6 +332,13 @@ def main():
             "output_bytes": (n * layer.out_h * layer.out_w * ((layer.out_c + 31) // 32) * 4),
             "roofline": {"bound": rb[0], "achieved": round(rb[1], 3), "peak": rb[2], "unit": rb[3],
                          "frac": round(rb[1] / rb[2], 4), "algorithmic_bytes": nbb}}
+    if not args.no_calibration:
+        cal = calibrate(pca, torch, stream)
+        line["calibration"] = cal
+        if bound == "alu":
+            mp = cal["popcount_peak"]["value"]
+            line["roofline"]["measured_peak"] = mp
+            line["roofline"]["frac_of_measured_peak"] = round(achieved / mp, 4)
     if args.cpu_images > 0:
         line["cpu_baseline"] = cpu_baseline(layer, inputs, min(args.cpu_images, n), args.cpu_repeats)
         if binary and layer.neuron in ("none", "relu"):
@@ -334,6 +347,47 @@ def main():
         line["cpu_baseline"] = None
     conv.close()
     print(json.dumps(line), flush=True)
+
+
+def calibrate(pca, torch, stream):
+    """Measured ceilings on this GPU: the popcount path's instruction pair
+    (v_xor_b32 + v_bcnt_u32_b32 on registers, 8 waves per SIMD, the library's
+    calibration kernel) in T bit-MAC/s, and a device-to-device copy of 1 GiB
+    (torch) in GB/s read + written.  Best of 5 timed runs each."""
+    simds = 4 * torch.cuda.get_device_properties(0).multi_processor_count
+    blocks, iters = 2 * simds, 4096  # 256-thread blocks: 8 waves per SIMD
+    sink = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
+    sptr = stream.cuda_stream
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    best = None
+    for i in range(6):
+        ev[0].record(stream)
+        pca.bconv_calibrate_popcount(sptr, blocks, iters, 1 + i, sink)
+        ev[1].record(stream)
+        ev[1].synchronize()
+        if i:  # the first run warms up
+            t = ev[0].elapsed_time(ev[1]) / 1e3
+            best = t if best is None else min(best, t)
+    bitmacs = blocks * 256 * iters * 8 * 32
+    src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    with torch.cuda.stream(stream):
+        dst.copy_(src)
+        tc = None
+        for _ in range(5):
+            ev[0].record(stream)
+            dst.copy_(src)
+            ev[1].record(stream)
+            ev[1].synchronize()
+            t = ev[0].elapsed_time(ev[1]) / 1e3
+            tc = t if tc is None else min(tc, t)
+    moved = 2 * src.numel() * 4
+    del src, dst, sink
+    return {"popcount_peak": {"value": round(bitmacs / best / 1e12, 3), "unit": "Tbit-MAC/s",
+                              "published": POPCOUNT_PEAK_TBITMAC, "kernel": "popc_peak_kernel",
+                              "work": f"{blocks} x 256 threads x {iters} rounds x 8 xor+bcnt pairs"},
+            "hbm_copy": {"value": round(moved / tc / 1e9, 1), "unit": "GB/s (read + write)",
+                         "published": HBM_PEAK_GBS, "bytes": moved}}
 
 
 def time_path(pca, torch, np, conv, n, x, stream, warmup, steps, bits=False):

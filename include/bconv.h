@@ -261,6 +261,22 @@ bconv_status_t bconv_forward_bits_profiled(bconv_t h, void *stream, int32_t n, c
  * string; "" for an invalid handle). */
 const char *bconv_main_kernel(bconv_t h, int32_t n);
 
+/* Calibration of the popcount path's instruction pair: launches `blocks`
+ * workgroups of 256 threads on `stream` (a hipStream_t; NULL = default
+ * stream); every thread runs `iters` rounds of eight independent
+ * v_xor_b32 + v_bcnt_u32_b32 pairs on register operands (no memory traffic),
+ * then writes one word to `sink` (device memory of blocks*256 uint32, owned by
+ * the caller).  Thread t's word is the sum over k = 0..7 of
+ *   iters * popcount(x[k % 4] ^ w_k),  w_k = (t * 2654435761) ^ (k * 0x9E3779B9),
+ *   x[0] = seed * 0x9E3779B1, x[1] = x[0] ^ 0x85EBCA77, x[2] = x[0] + 0xC2B2AE3D,
+ *   x[3] = x[0] ^ 0x27D4EB2F  (all mod 2^32),
+ * so a run does blocks*256*iters*8*32 bit-MACs, and timing it gives the VALU
+ * popcount rate the chip sustains (the convolution's two instructions per
+ * 32-bit word pair).  Asynchronous.  INVALID_ARGUMENT for blocks outside
+ * [1, 2^22], iters < 0 or a NULL sink. */
+bconv_status_t bconv_calibrate_popcount(void *stream, int32_t blocks, int32_t iters, uint32_t seed,
+                                        uint32_t *sink);
+
 /* Releases the handle's device memory.  The caller must make sure no queued
  * forward call still uses it.  NULL is accepted. */
 bconv_status_t bconv_destroy(bconv_t h);

@@ -19,7 +19,8 @@ from ._binding import (  # noqa: F401  (re-exported C ABI names)
     BCONV_ERR_UNSUPPORTED, BCONV_ERR_WORKSPACE, BCONV_FLAG_BETA_VALID_TAPS, BCONV_FLAG_INT8_MFMA, BCONV_FLAG_NONE,
     BCONV_FLAG_USE_BETA_SCALING,
     BCONV_NEURON_NONE, BCONV_NEURON_RELU, BCONV_OK, BCONV_XNOR, NEURON_CODES, TYPE_CODES,
-    BconvError, BconvLibraryMissing, bconv_create, bconv_create_fc, bconv_desc_t, bconv_destroy,
+    BconvError, BconvLibraryMissing, bconv_calibrate_popcount, bconv_create, bconv_create_fc, bconv_desc_t,
+    bconv_destroy,
     bconv_forward, bconv_forward_accum, bconv_forward_bits, bconv_forward_bits_profiled, bconv_forward_profiled,
     bconv_get_info, bconv_last_error,
     bconv_main_kernel, bconv_status_string, bconv_validate_desc, bconv_workspace_layout,

@@ -102,6 +102,7 @@ def load_library(path: Optional[str] = None):
         "bconv_forward_bits": (st, [vp, vp, i32, vp, vp, vp, sz]),
         "bconv_forward_bits_profiled": (st, [vp, vp, i32, vp, vp, vp, sz, vp, vp]),
         "bconv_main_kernel": (ctypes.c_char_p, [vp, i32]),
+        "bconv_calibrate_popcount": (st, [vp, i32, i32, u32, vp]),
         "bconv_destroy": (st, [vp]),
         "bconv_status_string": (ctypes.c_char_p, [st]),
         "bconv_last_error": (ctypes.c_char_p, []),
@@ -236,6 +237,10 @@ def bconv_forward_bits_profiled(h: int, stream, n: int, inp, out_bits, workspace
 
 def bconv_main_kernel(h: int, n: int) -> str:
     return load_library().bconv_main_kernel(h, n).decode()
+
+
+def bconv_calibrate_popcount(stream, blocks: int, iters: int, seed: int, sink) -> None:
+    _check(load_library().bconv_calibrate_popcount(_ptr(stream), blocks, iters, seed, _ptr(sink)))
 
 
 def bconv_destroy(h: int) -> None:

@@ -19,7 +19,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbconv.so")
 # longest compiles first, so they start before the pool fills
 SOURCES = ("xconv_k3.hip", "xconv_k24.hip", "xconv_k5.hip", "xconv_k1.hip", "bwmma.hip", "i8mma.hip", "gemm.hip",
-           "xconv.hip", "bwconv.hip", "bconv.hip", "pack.hip", "prepack.hip")
+           "xconv.hip", "bwconv.hip", "bconv.hip", "pack.hip", "prepack.hip", "calib.hip")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

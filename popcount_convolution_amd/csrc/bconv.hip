@@ -496,6 +496,16 @@ bconv_status_t bconv_forward_bits_profiled(bconv_t h, void *stream, int32_t n, c
                         main_end);
 }
 
+bconv_status_t bconv_calibrate_popcount(void *stream, int32_t blocks, int32_t iters, uint32_t seed, uint32_t *sink)
+{
+    if (blocks < 1 || blocks > (1 << 22) || iters < 0)
+        return fail(BCONV_ERR_INVALID_ARGUMENT, "blocks must be in [1, 2^22] and iters >= 0");
+    if (!sink) return fail(BCONV_ERR_INVALID_ARGUMENT, "sink is NULL");
+    const hipError_t e = bconv::launch_popc_peak(static_cast<hipStream_t>(stream), blocks, iters, seed, sink);
+    if (e != hipSuccess) return hip_fail(e, "calibration kernel");
+    return BCONV_OK;
+}
+
 const char *bconv_main_kernel(bconv_t h, int32_t n)
 {
     if (!h || n < 0) return "";

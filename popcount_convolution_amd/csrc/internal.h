@@ -231,6 +231,9 @@ hipError_t launch_prepack_i8(const Geom &g, hipStream_t s, const uint32_t *user_
 hipError_t launch_pack_i8(const Geom &g, hipStream_t s, const float *x, const float *in_scale, const float *in_bias,
                           int and_mode, int8_t *act, float *a_map);
 const char *i8mma_kernel_name();
+// Calibration kernel: blocks x 256 lanes, each running iters rounds of eight
+// v_xor_b32 + v_bcnt_u32_b32 pairs on registers; one sum per lane to sink.
+hipError_t launch_popc_peak(hipStream_t stream, int blocks, int iters, uint32_t seed, uint32_t *sink);
 hipError_t launch_i8mma(const Geom &g, const Launch &L, const int8_t *act, const void *frag, const Epilogue &e,
                         float *out, int32_t *acc_out);
 

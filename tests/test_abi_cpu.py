@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_header_symbols_exported(lib):
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     raw = ctypes.CDLL(_binding.LIB_PATH)
     missing = [n for n in names if not hasattr(raw, n)]
     assert not missing, missing
@@ -127,3 +127,11 @@ def test_measured_layer_shapes():
     assert L[4].is_fc and (L[4].out_h, L[4].out_w) == (1, 1)
     assert L[4].nominal_macs() == 256 * 4096 * 25088
     assert L[1].nominal_macs() == 3_699_376_128
+
+
+def test_calibration_argument_errors(lib):
+    """Argument errors of the calibration entry point come back before any launch."""
+    for blocks, iters, sink in ((0, 1, 0x1000), (1 << 23, 1, 0x1000), (1, -1, 0x1000), (1, 1, None)):
+        with pytest.raises(pca.BconvError) as e:
+            pca.bconv_calibrate_popcount(None, blocks, iters, 1, sink)
+        assert e.value.status == pca.BCONV_ERR_INVALID_ARGUMENT

@@ -577,6 +577,26 @@ def test_maximum_window_is_exact(dev):
         assert np.all(got["out"] == np.float32(1 << 23)), form
 
 
+def test_calibration_kernel(dev):
+    """The popcount calibration kernel does the work its header states: each
+    thread's word is sum_k iters * popcount(x[k % 4] ^ w_k), computed here with
+    Python integers."""
+    blocks, iters, seed = 6, 37, 12345
+    sink = torch.zeros(blocks * 256, dtype=torch.int32, device=dev)
+    pca.bconv_calibrate_popcount(torch.cuda.current_stream().cuda_stream, blocks, iters, seed, sink)
+    torch.cuda.synchronize()
+    got = sink.cpu().numpy().view(np.uint32)
+    m = 0xFFFFFFFF
+    x0 = (seed * 0x9E3779B1) & m
+    xs = [x0, x0 ^ 0x85EBCA77, (x0 + 0xC2B2AE3D) & m, x0 ^ 0x27D4EB2F]
+    for t in range(blocks * 256):
+        want = 0
+        for k in range(8):
+            w = ((t * 2654435761) & m) ^ ((k * 0x9E3779B9) & m)
+            want += iters * bin(xs[k % 4] ^ w).count("1")
+        assert int(got[t]) == want & m, t
+
+
 def test_argument_errors(dev):
     layer = workloads.BENCH_LAYER.with_(n=2)
     inputs = workloads.make_inputs(layer, 5)
