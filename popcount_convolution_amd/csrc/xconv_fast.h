@@ -259,16 +259,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void x
             for (int col = 0; col < NCOL; ++col)
 #pragma unroll
                 for (int j = 0; j < CWC; ++j) x[col * CWC + j] = bits[base + col * CW + ch * CWC + j];
+            // Word pairs in runs of the strip's P pixels: P xor/and into
+            // separate temporaries, then P counts into the P accumulators.
+            // The VALU issues long runs of one instruction faster than
+            // alternating dependent pairs (about 3.7 against 4.4 cycles per
+            // wave64 instruction, measured); the scheduling barriers keep the
+            // runs, and the count is written as the accumulating instruction
+            // itself so the compiler cannot split it into a count and an add.
 #pragma unroll
-            for (int p = 0; p < P; ++p)
+            for (int kx = 0; kx < KW; ++kx)
 #pragma unroll
-                for (int kx = 0; kx < KW; ++kx)
+                for (int j = 0; j < CWC; ++j) {
+                    const uint32_t wv = w[kx * CW + ch * CWC + j];
+                    uint32_t t[P];
 #pragma unroll
-                    for (int j = 0; j < CWC; ++j) {
+                    for (int p = 0; p < P; ++p) {
                         const uint32_t xv = x[(p * SW + kx) * CWC + j];
-                        const uint32_t wv = w[kx * CW + ch * CWC + j];
-                        acc[p] += __builtin_popcount(AND ? (xv & wv) : (xv ^ wv));
+                        t[p] = AND ? (xv & wv) : (xv ^ wv);
                     }
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int p = 0; p < P; ++p) asm("v_bcnt_u32_b32 %0, %1, %0" : "+v"(acc[p]) : "v"(t[p]));
+                    __builtin_amdgcn_sched_barrier(0);
+                }
         }
     }
 
