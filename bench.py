@@ -438,16 +438,19 @@ KERNEL_FILES = {"xconv_fast": "xconv_fast.h", "xconv_generic": "xconv.hip", "bge
 
 
 def _kernel_sha(kernel: str) -> str:
-    """Hash of the sources a main kernel is built from (its own file and the
-    shared internal header): recorded traffic stays valid while it matches."""
+    """Hash of the code a main kernel is built from (its own file and the
+    shared internal header, comments and whitespace removed): recorded
+    traffic stays valid while it matches."""
     import hashlib
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "popcount_convolution_amd", "csrc")
     base = kernel.split("<")[0]
     prefix = next(p for p in KERNEL_FILES if base.startswith(p))
     for name in (KERNEL_FILES[prefix], "internal.h"):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
+        with open(os.path.join(csrc, name)) as f:
+            code = re.sub(r"//[^\n]*|/\*.*?\*/", " ", f.read(), flags=re.S)
+        h.update(name.encode() + " ".join(code.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -10,13 +10,17 @@
 //   AND:  popcount(x & w) per word.
 // followed by the fused epilogue  neuron(v*scale[c]*beta + bias[c]).
 //
-// Mapping on gfx950: a wave owns 64 output channels (one per lane).  Each
-// lane keeps its channel's whole weight window in VGPRs.  The binarised
-// input words of a strip of P neighbouring output pixels are the same for
-// every lane, so they are fetched with scalar loads into SGPRs and fed to
-// v_xor_b32 / v_and_b32 as the scalar operand; v_bcnt_u32_b32 then counts and
-// accumulates in one instruction.  Two VALU instructions per word pair, no LDS
-// and no vector loads in the inner loop.
+// Mapping on gfx950: a wave owns 64 output channels (one per lane) of a
+// strip of P neighbouring output pixels.  Kernel rows are walked in order;
+// for each, every lane loads its channel's weight words of that row into
+// VGPRs (16-byte loads from an L1/L2-resident table), and the binarised input
+// words of the strip, the same for every lane, are fetched with scalar loads
+// into SGPRs and fed to v_xor_b32 / v_and_b32 as the scalar operand;
+// v_bcnt_u32_b32 then counts and accumulates in one instruction.  Two VALU
+// instructions per word pair, issued in runs of P of each (see the row loop),
+// no LDS.  Strips are numbered down image columns and dealt to the XCDs in
+// contiguous ranges, so the waves running together share input rows in the
+// caches.
 #pragma once
 
 #include "internal.h"
@@ -24,7 +28,6 @@
 #include <type_traits>
 
 namespace bconv {
-
 
 typedef const uint32_t __attribute__((address_space(4))) *scalar_u32_ptr;
 typedef const float __attribute__((address_space(4))) *scalar_f32_ptr;
