@@ -257,6 +257,27 @@ bconv_status_t bconv_forward_bits_profiled(bconv_t h, void *stream, int32_t n, c
                                            size_t workspace_bytes, void *main_begin,
                                            void *main_end);
 
+/* Forward pass from input that is already binarised and packed, as a previous
+ * layer's bconv_forward_bits writes it (Apple "MPSCNNBinaryConvolution",
+ * Overview: under XNOR and AND only the sign of each input value enters the
+ * product, so the sign bits are the whole input).  `in_bits` is device memory
+ * of n*in_h*in_w*ceil(in_c/32) uint32 words, NHWC, channel c of pixel (b, y, x)
+ * being bit c % 32 of word ((b*in_h + y)*in_w + x)*ceil(in_c/32) + c/32; a 1
+ * stands for an input >= 0 (+1 under XNOR, 1 under AND), a 0 for an input
+ * < 0 (-1 under XNOR, 0 under AND).  Bits past in_c are ignored.  The result
+ * equals bconv_forward on any fp32 input with those signs.  Workspace as for
+ * bconv_forward.  UNSUPPORTED (checked before n) for handles that read the
+ * full-precision input: binaryWeights, beta scaling, an input scale or bias,
+ * BCONV_FLAG_INT8_MFMA.  Otherwise the errors of bconv_forward. */
+bconv_status_t bconv_forward_packed(bconv_t h, void *stream, int32_t n, const uint32_t *in_bits,
+                                    float *out, void *workspace, size_t workspace_bytes);
+
+/* As bconv_forward_packed, writing packed sign bits as bconv_forward_bits does,
+ * so binary layers chain on bits alone. */
+bconv_status_t bconv_forward_packed_bits(bconv_t h, void *stream, int32_t n,
+                                         const uint32_t *in_bits, uint32_t *out_bits,
+                                         void *workspace, size_t workspace_bytes);
+
 /* Name of the kernel bconv_forward_profiled brackets for batch n (a static
  * string; "" for an invalid handle). */
 const char *bconv_main_kernel(bconv_t h, int32_t n);

@@ -21,7 +21,8 @@ from ._binding import (  # noqa: F401  (re-exported C ABI names)
     BCONV_NEURON_NONE, BCONV_NEURON_RELU, BCONV_OK, BCONV_XNOR, NEURON_CODES, TYPE_CODES,
     BconvError, BconvLibraryMissing, bconv_calibrate_popcount, bconv_create, bconv_create_fc, bconv_desc_t,
     bconv_destroy,
-    bconv_forward, bconv_forward_accum, bconv_forward_bits, bconv_forward_bits_profiled, bconv_forward_profiled,
+    bconv_forward, bconv_forward_accum, bconv_forward_bits, bconv_forward_bits_profiled, bconv_forward_packed,
+    bconv_forward_packed_bits, bconv_forward_profiled,
     bconv_get_info, bconv_last_error,
     bconv_main_kernel, bconv_status_string, bconv_validate_desc, bconv_workspace_layout,
     bconv_workspace_size, load_library, make_desc)
@@ -121,6 +122,21 @@ class BinaryConvolution:
         bconv_forward_bits(self.handle, self._stream(stream), n, x, out_bits, workspace,
                            workspace.numel() * workspace.element_size())
         return out_bits
+
+    def forward_packed(self, x_bits, out=None, workspace=None, stream=None, bits_out=False):
+        """Forward pass from packed input sign bits (see bconv_forward_packed):
+        int32 words [n, in_h, in_w, ceil(in_c/32)], e.g. a previous layer's
+        forward_bits.  Returns fp32 NHWC, or packed output bits with bits_out."""
+        import torch
+        n = x_bits.shape[0]
+        if out is None:
+            shape = (n, self.out_h, self.out_w, self.out_words() if bits_out else self.out_c)
+            out = torch.empty(shape, dtype=torch.int32 if bits_out else torch.float32, device=x_bits.device)
+        if workspace is None:
+            workspace = self.workspace(n, x_bits.device)
+        fn = bconv_forward_packed_bits if bits_out else bconv_forward_packed
+        fn(self.handle, self._stream(stream), n, x_bits, out, workspace, workspace.numel() * workspace.element_size())
+        return out
 
     def main_kernel(self, n: int) -> str:
         return bconv_main_kernel(self.handle, n)

@@ -102,6 +102,8 @@ def load_library(path: Optional[str] = None):
         "bconv_forward_bits": (st, [vp, vp, i32, vp, vp, vp, sz]),
         "bconv_forward_bits_profiled": (st, [vp, vp, i32, vp, vp, vp, sz, vp, vp]),
         "bconv_main_kernel": (ctypes.c_char_p, [vp, i32]),
+        "bconv_forward_packed": (st, [vp, vp, i32, vp, vp, vp, sz]),
+        "bconv_forward_packed_bits": (st, [vp, vp, i32, vp, vp, vp, sz]),
         "bconv_calibrate_popcount": (st, [vp, i32, i32, u32, vp]),
         "bconv_destroy": (st, [vp]),
         "bconv_status_string": (ctypes.c_char_p, [st]),
@@ -233,6 +235,16 @@ def bconv_forward_bits_profiled(h: int, stream, n: int, inp, out_bits, workspace
     _check(load_library().bconv_forward_bits_profiled(h, _ptr(stream), n, _ptr(inp), _ptr(out_bits),
                                                       _ptr(workspace), workspace_bytes,
                                                       _ptr(main_begin), _ptr(main_end)))
+
+
+def bconv_forward_packed(h: int, stream, n: int, in_bits, out, workspace, workspace_bytes: int) -> None:
+    _check(load_library().bconv_forward_packed(h, _ptr(stream), n, _ptr(in_bits), _ptr(out), _ptr(workspace),
+                                               workspace_bytes))
+
+
+def bconv_forward_packed_bits(h: int, stream, n: int, in_bits, out_bits, workspace, workspace_bytes: int) -> None:
+    _check(load_library().bconv_forward_packed_bits(h, _ptr(stream), n, _ptr(in_bits), _ptr(out_bits),
+                                                    _ptr(workspace), workspace_bytes))
 
 
 def bconv_main_kernel(h: int, n: int) -> str:

@@ -220,19 +220,36 @@ bool ranges_overlap(const void *a, size_t an, const void *b, size_t bn)
 // fp32 values ([n][out_h][out_w][ceil(out_c/32)] words).
 enum class Sink { Output, Accum, Bits };
 
-bconv_status_t forward_impl(bconv_t h, void *stream, int32_t n, const float *in, void *dst, Sink sink,
-                            void *workspace, size_t workspace_bytes, void *ev_begin, void *ev_end)
+// Input forms: fp32 NHWC values, or sign bits already packed in the layout
+// of the bit buffer without its halo ([n][in_h][in_w][ceil(in_c/32)] words).
+enum class Source { Values, Bits };
+
+bconv_status_t forward_impl(bconv_t h, void *stream, int32_t n, const void *src, Source source, void *dst,
+                            Sink sink, void *workspace, size_t workspace_bytes, void *ev_begin, void *ev_end)
 {
     if (!h) return fail(BCONV_ERR_INVALID_ARGUMENT, "handle is NULL");
     if (n < 0) return fail(BCONV_ERR_INVALID_ARGUMENT, "n must be >= 0");
+    if (source == Source::Bits) {
+        // Packed bits carry only the signs: every step that reads the
+        // full-precision input is out of reach.
+        if (h->type == BCONV_BINARY_WEIGHTS)
+            return fail(BCONV_ERR_UNSUPPORTED, "binaryWeights multiplies the full-precision input, not its sign");
+        if (uses_beta(h))
+            return fail(BCONV_ERR_UNSUPPORTED, "beta needs |input|, which packed sign bits do not carry");
+        if (h->d_in_scale || h->d_in_bias)
+            return fail(BCONV_ERR_UNSUPPORTED, "the input scale and bias apply before the sign");
+        if (h->i8) return fail(BCONV_ERR_UNSUPPORTED, "the int8 matrix-core path takes fp32 input only");
+    }
     if (n == 0) return BCONV_OK;
-    if (!in || !dst) return fail(BCONV_ERR_INVALID_ARGUMENT, "in/out must not be NULL");
+    if (!src || !dst) return fail(BCONV_ERR_INVALID_ARGUMENT, "in/out must not be NULL");
     const bconv_desc_t &d = h->desc;
-    const size_t in_bytes = (size_t)n * d.in_h * d.in_w * d.in_c * 4;
+    const float *in = source == Source::Values ? static_cast<const float *>(src) : nullptr;
+    const size_t in_bytes =
+        (size_t)n * d.in_h * d.in_w * (source == Source::Bits ? (size_t)((d.in_c + 31) / 32) : (size_t)d.in_c) * 4;
     const int out_words = (d.out_c + 31) / 32;
     const size_t out_bytes =
         (size_t)n * h->out_h * h->out_w * (sink == Sink::Bits ? (size_t)out_words : (size_t)d.out_c) * 4;
-    if (ranges_overlap(in, in_bytes, dst, out_bytes))
+    if (ranges_overlap(src, in_bytes, dst, out_bytes))
         return fail(BCONV_ERR_INVALID_ARGUMENT, "input and output overlap");
     if ((long long)n * d.in_h * d.in_w >= (1LL << 31) || (long long)n * h->out_h * h->out_w * h->tiles >= (1LL << 29) ||
         in_bytes >= (size_t)0x7fffffff || out_bytes >= (size_t)0x7fffffff)
@@ -242,7 +259,7 @@ bconv_status_t forward_impl(bconv_t h, void *stream, int32_t n, const float *in,
     if (L.total_bytes > 0 && (!workspace || workspace_bytes < L.total_bytes))
         return fail(BCONV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total_bytes,
                     workspace ? workspace_bytes : (size_t)0);
-    if (L.total_bytes > 0 && (ranges_overlap(workspace, L.total_bytes, in, in_bytes) ||
+    if (L.total_bytes > 0 && (ranges_overlap(workspace, L.total_bytes, src, in_bytes) ||
                               ranges_overlap(workspace, L.total_bytes, dst, out_bytes)))
         return fail(BCONV_ERR_INVALID_ARGUMENT, "workspace overlaps input or output");
 
@@ -256,7 +273,10 @@ bconv_status_t forward_impl(bconv_t h, void *stream, int32_t n, const float *in,
     float *beta = L.beta_offset == SIZE_MAX ? nullptr : reinterpret_cast<float *>(ws + L.beta_offset);
 
     hipError_t e;
-    if (h->i8) {
+    if (source == Source::Bits) {
+        e = bconv::launch_repad(g, s, static_cast<const uint32_t *>(src), bits);
+        if (e != hipSuccess) return hip_fail(e, "repad kernel");
+    } else if (h->i8) {
         e = bconv::launch_pack_i8(g, s, in, h->d_in_scale, h->d_in_bias, h->type == BCONV_AND,
                                   reinterpret_cast<int8_t *>(bits), a_map);
         if (e != hipSuccess) return hip_fail(e, "int8 pack kernel");
@@ -465,35 +485,52 @@ bconv_status_t bconv_workspace_layout(bconv_t h, int32_t n, bconv_workspace_layo
 bconv_status_t bconv_forward(bconv_t h, void *stream, int32_t n, const float *in, float *out,
                              void *workspace, size_t workspace_bytes)
 {
-    return forward_impl(h, stream, n, in, out, Sink::Output, workspace, workspace_bytes, nullptr, nullptr);
+    return forward_impl(h, stream, n, in, Source::Values, out, Sink::Output, workspace, workspace_bytes, nullptr,
+                        nullptr);
 }
 
 bconv_status_t bconv_forward_accum(bconv_t h, void *stream, int32_t n, const float *in, void *acc,
                                    void *workspace, size_t workspace_bytes)
 {
-    return forward_impl(h, stream, n, in, acc, Sink::Accum, workspace, workspace_bytes, nullptr, nullptr);
+    return forward_impl(h, stream, n, in, Source::Values, acc, Sink::Accum, workspace, workspace_bytes, nullptr,
+                        nullptr);
 }
 
 bconv_status_t bconv_forward_profiled(bconv_t h, void *stream, int32_t n, const float *in, float *out,
                                       void *workspace, size_t workspace_bytes, void *main_begin,
                                       void *main_end)
 {
-    return forward_impl(h, stream, n, in, out, Sink::Output, workspace, workspace_bytes, main_begin,
+    return forward_impl(h, stream, n, in, Source::Values, out, Sink::Output, workspace, workspace_bytes, main_begin,
                         main_end);
 }
 
 bconv_status_t bconv_forward_bits(bconv_t h, void *stream, int32_t n, const float *in, uint32_t *out_bits,
                                   void *workspace, size_t workspace_bytes)
 {
-    return forward_impl(h, stream, n, in, out_bits, Sink::Bits, workspace, workspace_bytes, nullptr, nullptr);
+    return forward_impl(h, stream, n, in, Source::Values, out_bits, Sink::Bits, workspace, workspace_bytes,
+                        nullptr, nullptr);
 }
 
 bconv_status_t bconv_forward_bits_profiled(bconv_t h, void *stream, int32_t n, const float *in,
                                            uint32_t *out_bits, void *workspace, size_t workspace_bytes,
                                            void *main_begin, void *main_end)
 {
-    return forward_impl(h, stream, n, in, out_bits, Sink::Bits, workspace, workspace_bytes, main_begin,
+    return forward_impl(h, stream, n, in, Source::Values, out_bits, Sink::Bits, workspace, workspace_bytes, main_begin,
                         main_end);
+}
+
+bconv_status_t bconv_forward_packed(bconv_t h, void *stream, int32_t n, const uint32_t *in_bits, float *out,
+                                    void *workspace, size_t workspace_bytes)
+{
+    return forward_impl(h, stream, n, in_bits, Source::Bits, out, Sink::Output, workspace, workspace_bytes, nullptr,
+                        nullptr);
+}
+
+bconv_status_t bconv_forward_packed_bits(bconv_t h, void *stream, int32_t n, const uint32_t *in_bits,
+                                         uint32_t *out_bits, void *workspace, size_t workspace_bytes)
+{
+    return forward_impl(h, stream, n, in_bits, Source::Bits, out_bits, Sink::Bits, workspace, workspace_bytes,
+                        nullptr, nullptr);
 }
 
 bconv_status_t bconv_calibrate_popcount(void *stream, int32_t blocks, int32_t iters, uint32_t seed, uint32_t *sink)

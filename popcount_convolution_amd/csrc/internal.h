@@ -193,6 +193,9 @@ __device__ __forceinline__ int window_valid_taps(int oy, int ox, int sh, int sw,
 // Launchers (each returns the hipGetLastError() of its launch).
 hipError_t launch_pack(const Geom &g, hipStream_t s, const float *x, const float *in_scale,
                        const float *in_bias, uint32_t *bits, float *a_map);
+// Copies caller-packed input bits ([n][in_h][in_w][words]) into the padded bit
+// buffer, zeroing the halo, the slack and the bits past in_c.
+hipError_t launch_repad(const Geom &g, hipStream_t s, const uint32_t *src, uint32_t *bits);
 hipError_t launch_prepack(const Geom &g, hipStream_t s, const uint32_t *user_bits, uint32_t *lane_words,
                           int32_t *lane_popc, float *pm_weights, int pm_cols, int type);
 // Returns true when a specialised convolution kernel exists for this shape.

@@ -5,6 +5,8 @@
 // equation (mean over channels of |in'|).  The A map is written with the
 // same zero halo as the bit buffer, so the convolution kernels form beta (the
 // window sum of A over kh*kw, first beta equation) without bounds checks.
+// The repad kernel at the end serves input that arrives already packed (a
+// previous layer's sign bits): it only moves words into the padded buffer.
 #include "internal.h"
 
 namespace bconv {
@@ -368,6 +370,68 @@ hipError_t launch_pack(const Geom &g, hipStream_t s, const float *x, const float
     case 32: return launch_pack_t<1, 32>(a, pack_blocks, halo_blocks, s);
     default: return launch_pack_t<1, 64>(a, pack_blocks, halo_blocks, s);
     }
+}
+
+namespace {
+
+struct RepadArgs {
+    const uint32_t *src;    // [n][in_h][in_w][words]
+    uint32_t *bits;         // padded [n][rows][cols][words] + slack
+    unsigned image_words;   // rows*cols*words
+    unsigned total;         // n*image_words + slack (< 2^31, checked by the host)
+    unsigned image_count;   // n
+    int in_h, in_w, words, cols, halo_h, halo_w;
+    uint32_t tail_mask;     // valid bits of a pixel's last word
+};
+
+// One thread per word of the padded buffer: the caller's word where the pixel
+// is inside the image (the last word of a pixel masked to in_c bits), else 0
+// (halo and the slack after the last image).  Consecutive threads read
+// consecutive words of an image row.
+__global__ __launch_bounds__(256) void repad_kernel(RepadArgs a)
+{
+    const unsigned t = blockIdx.x * 256u + threadIdx.x;
+    if (t >= a.total) return;
+    uint32_t v = 0;
+    const unsigned img = t / a.image_words;
+    if (img < a.image_count) {
+        const unsigned r = t - img * a.image_words;
+        const unsigned pix = r / (unsigned)a.words;
+        const unsigned w = r - pix * (unsigned)a.words;
+        const unsigned row = pix / (unsigned)a.cols;
+        const unsigned col = pix - row * (unsigned)a.cols;
+        const int y = (int)row - a.halo_h, x = (int)col - a.halo_w;
+        if (y >= 0 && y < a.in_h && x >= 0 && x < a.in_w) {
+            v = a.src[(((unsigned long long)img * a.in_h + y) * a.in_w + x) * a.words + w];
+            if ((int)w == a.words - 1) v &= a.tail_mask;
+        }
+    }
+    store_through(&a.bits[t], v);
+}
+
+}  // namespace
+
+hipError_t launch_repad(const Geom &g, hipStream_t s, const uint32_t *src, uint32_t *bits)
+{
+    const long long image_words = (long long)g.bits_rows * g.bits_cols * g.words;
+    const long long total = (long long)g.n * image_words + g.bits_slack_words;
+    if (g.n <= 0) return hipSuccess;
+    if (total >= 0x7fffffffLL) return hipErrorInvalidValue;
+    RepadArgs a{};
+    a.src = src;
+    a.bits = bits;
+    a.image_words = (unsigned)image_words;
+    a.total = (unsigned)total;
+    a.image_count = (unsigned)g.n;
+    a.in_h = g.in_h;
+    a.in_w = g.in_w;
+    a.words = g.words;
+    a.cols = g.bits_cols;
+    a.halo_h = g.bits_halo_h;
+    a.halo_w = g.bits_halo_w;
+    a.tail_mask = g.in_c % 32 ? (1u << (g.in_c % 32)) - 1u : 0xffffffffu;
+    hipLaunchKernelGGL(repad_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a);
+    return hipGetLastError();
 }
 
 }  // namespace bconv

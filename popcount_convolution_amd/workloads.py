@@ -151,6 +151,17 @@ def make_inputs(layer: Layer, seed: int, n: Optional[int] = None) -> dict:
     return out
 
 
+def make_packed_input(layer: Layer, seed: int, n: Optional[int] = None) -> np.ndarray:
+    """Uniformly random uint32 words [n,H,W,ceil(Cin/32)] standing for packed
+    input sign bits (bit c%32 of word c//32 is channel c).  The bits past Cin
+    are random as well: a consumer must ignore them."""
+    n = layer.n if n is None else n
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(seed)
+    words = torch.randint(0, 2 ** 32, (n, layer.in_h, layer.in_w, layer.words), generator=gen, dtype=torch.int64)
+    return np.ascontiguousarray(words.numpy().astype(np.uint32))
+
+
 def layer_seed(index: int) -> int:
     """Seed of measured layer ``index``."""
     return 1000 + index

@@ -164,6 +164,13 @@ def unpack_words(words: np.ndarray, nbits: int) -> np.ndarray:
     return b[..., :nbits] if nbits is not None else b
 
 
+def values_from_bits(words: np.ndarray, nbits: int) -> np.ndarray:
+    """The fp32 input that packed sign bits stand for: +1 where the bit is 1
+    and -1 where it is 0 (any input with these signs gives the same layer
+    output under XNOR and AND); bits past ``nbits`` are dropped."""
+    return np.where(unpack_words(words, nbits) != 0, 1.0, -1.0).astype(np.float32)
+
+
 def compare_bits(layer: workloads.Layer, inputs: dict, words: np.ndarray, ref: dict = None, images=None):
     """Packed sign bits of the output against the oracle: bit = !(y < 0).  The
     sign is decided by the fp32 value, so positions whose oracle value lies

@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_header_symbols_exported(lib):
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 18, names
     raw = ctypes.CDLL(_binding.LIB_PATH)
     missing = [n for n in names if not hasattr(raw, n)]
     assert not missing, missing
@@ -98,6 +98,8 @@ def test_null_handle_calls(lib):
     assert lib.bconv_destroy(None) == pca.BCONV_OK
     assert lib.bconv_get_info(None, None, None, None, None) == pca.BCONV_ERR_INVALID_ARGUMENT
     assert lib.bconv_main_kernel(None, 1) == b""
+    for fn in (lib.bconv_forward_packed, lib.bconv_forward_packed_bits):
+        assert fn(None, None, 1, None, None, None, 0) == pca.BCONV_ERR_INVALID_ARGUMENT
 
 
 def test_missing_library_fails_loudly():

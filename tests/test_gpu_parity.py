@@ -465,6 +465,187 @@ def test_forward_bits_measured_layer(dev, index):
     parity.compare_bits(layer, inputs, words, images=np.array(images))
 
 
+# ------------------------------------------------ packed sign-bit input
+
+def _packed_layers():
+    base = workloads.Layer("packed", "xnor", 2, 14, 14, 128, 128, 3, 3, 1, 1, 1, 1)
+    geoms = [
+        dict(name="packed_xnor_k3_c128"),
+        dict(name="packed_and_k3_c256_o70", type="and", in_c=256, out_c=70, obias_dist=("normal", -20.0, 5.0)),
+        dict(name="packed_xnor_tail_c100_o33", n=3, in_h=11, in_w=19, in_c=100, out_c=33, neuron="relu"),
+        dict(name="packed_and_tail_c37_s2", type="and", in_h=13, in_w=9, in_c=37, out_c=40, stride_h=2,
+             stride_w=2),
+        dict(name="packed_fc_c37_o66", n=5, in_h=4, in_w=5, in_c=37, out_c=66, kernel_h=4, kernel_w=5, pad_h=0,
+             pad_w=0),
+        dict(name="packed_xnor_k5_p2_c64", in_c=64, out_c=64, kernel_h=5, kernel_w=5, pad_h=2, pad_w=2),
+        dict(name="packed_xnor_k1_c64_o96", in_c=64, out_c=96, kernel_h=1, kernel_w=1, pad_h=0, pad_w=0),
+        dict(name="packed_and_k2x4_asym", type="and", in_c=32, out_c=64, kernel_h=2, kernel_w=4, pad_h=1, pad_w=2,
+             pad_bottom=0, pad_right=1),
+        dict(name="packed_xnor_1px_c1", n=1, in_h=1, in_w=1, in_c=1, out_c=5),
+    ]
+    return [base.with_(**g) for g in geoms]
+
+
+PACKED_LAYERS = _packed_layers()
+
+
+def _packed_run(layer, inputs, words, dev, generic=False):
+    """forward_packed (fp32 and bits) of `words` on a workspace poisoned with
+    0xA5, and forward / forward_accum of the +-1 values the words stand for, on
+    one handle.  Also returns the padded bit buffer the repad kernel wrote."""
+    values = parity.values_from_bits(words, layer.in_c)
+    with parity.force_generic(generic):
+        conv = pca.BinaryConvolution.from_layer(layer, inputs)
+    try:
+        n = words.shape[0]
+        w = torch.from_numpy(words.view(np.int32)).to(dev)
+        x = torch.from_numpy(values).to(dev)
+        shape = (n, conv.out_h, conv.out_w, conv.out_c)
+        ws = conv.workspace(n, dev)
+        ws.fill_(0xA5)
+        out = torch.full(shape, float("nan"), dtype=torch.float32, device=dev)
+        conv.forward_packed(w, out, ws)
+        torch.cuda.synchronize()
+        L = pca.bconv_workspace_layout(conv.handle, n)
+        cnt = n * L["bits_rows"] * L["bits_cols"] * L["bits_words"]
+        padded = ws.cpu().numpy()[L["bits_offset"]:L["bits_offset"] + 4 * cnt].view("<u4") \
+            .reshape(n, L["bits_rows"], L["bits_cols"], L["bits_words"])
+        ws.fill_(0xA5)
+        out_bits = conv.forward_packed(w, workspace=ws, bits_out=True)
+        ref_out = conv.forward(x)
+        acc = conv.forward_accum(x)
+        torch.cuda.synchronize()
+        return dict(out=out.cpu().numpy(), bits=out_bits.cpu().numpy(), values=values,
+                    via_values=ref_out.cpu().numpy(), acc=acc.cpu().numpy(), padded=padded,
+                    pad=(L["bits_pad_h"], L["bits_pad_w"]), kernel=conv.main_kernel(n))
+    finally:
+        conv.close()
+
+
+def _check_packed(layer, inputs, words, r, images=None):
+    """The packed-input results against the oracle on the +-1 values."""
+    sub = dict(inputs, x=r["values"])
+    assert np.array_equal(r["out"].view(np.uint32), r["via_values"].view(np.uint32)), \
+        f"{r['kernel']}: packed input and fp32 input with the same signs give different outputs"
+    parity.compare(layer, sub, {"out": r["out"], "acc": r["acc"]}, images=images, workspace=False)
+    got = parity.unpack_words(r["bits"], layer.out_c)
+    assert np.array_equal(got, (~(r["out"] < 0)).astype(np.uint8)), f"{r['kernel']}: output bits differ"
+    assert not parity.unpack_words(r["bits"], None)[..., layer.out_c:].any(), "output bits past out_c are set"
+    ph, pw = r["pad"]
+    h, w = layer.in_h, layer.in_w
+    inner = r["padded"][:, ph:ph + h, pw:pw + w, :]
+    mask = np.full(layer.words, 0xFFFFFFFF, np.uint32)
+    if layer.in_c % 32:
+        mask[-1] = (1 << (layer.in_c % 32)) - 1
+    assert np.array_equal(inner, words & mask), f"{layer.name}: repadded bits differ from the masked input"
+    halo = r["padded"].copy()
+    halo[:, ph:ph + h, pw:pw + w, :] = 0
+    assert not halo.any(), f"{layer.name}: halo of the repadded input is not zero"
+
+
+@pytest.mark.parametrize("generic", [False, True], ids=["fast", "generic"])
+@pytest.mark.parametrize("layer", PACKED_LAYERS, ids=[l.name for l in PACKED_LAYERS])
+def test_forward_packed(dev, layer, generic):
+    """bconv_forward_packed / _bits on random words (tail bits past in_c random
+    too): the oracle's result on the +-1 input those bits stand for, and
+    bit-identical to bconv_forward on that input."""
+    seed = 8600 + PACKED_LAYERS.index(layer)
+    inputs = workloads.make_inputs(layer, seed)
+    words = workloads.make_packed_input(layer, seed + 50)
+    _log(f"packed {layer.name} generic={generic}")
+    r = _packed_run(layer, inputs, words, dev, generic=generic)
+    _check_packed(layer, inputs, words, r)
+
+
+PACKED_MEASURED = [i for i, l in enumerate(workloads.LAYERS)
+                   if l.type != "binary_weights" and not l.use_beta and l.iscale_dist is None]
+
+
+@pytest.mark.parametrize("index", PACKED_MEASURED, ids=[workloads.LAYERS[i].name for i in PACKED_MEASURED])
+def test_forward_packed_measured_layer(dev, index):
+    """Packed input on each measured layer it applies to, at full size (oracle
+    on sampled images)."""
+    layer = workloads.LAYERS[index]
+    inputs = workloads.make_inputs(layer, workloads.layer_seed(index))
+    words = workloads.make_packed_input(layer, workloads.layer_seed(index) + 77)
+    _log(f"packed layer {layer.name}")
+    r = _packed_run(layer, inputs, words, dev)
+    n = layer.n
+    _check_packed(layer, inputs, words, r, images=np.array(sorted({0, n // 2, n - 1})))
+
+
+def test_packed_chain(dev):
+    """Two binary layers on bits alone: the first writes packed output sign bits
+    (bconv_forward_bits), the second reads them (bconv_forward_packed_bits and
+    bconv_forward_packed).  The second layer's result is the oracle's on the
+    +-1 input the first layer's bits stand for."""
+    l1 = workloads.Layer("chain_xnor", "xnor", 2, 15, 13, 96, 128, 3, 3, 1, 1, 1, 1,
+                         obias_dist=("normal", 0.0, 5.0))
+    l2 = workloads.Layer("chain_and_s2", "and", 2, 15, 13, 128, 70, 3, 3, 2, 2, 1, 1)
+    l3 = workloads.Layer("chain_fc", "xnor", 2, 8, 7, 70, 10, 8, 7, 1, 1, 0, 0)
+    in1, in2, in3 = (workloads.make_inputs(l, 8700 + k) for k, l in enumerate((l1, l2, l3)))
+    c1, c2, c3 = (pca.BinaryConvolution.from_layer(l, i) for l, i in ((l1, in1), (l2, in2), (l3, in3)))
+    try:
+        x = torch.from_numpy(in1["x"]).to(dev)
+        b1 = c1.forward_bits(x)
+        b2 = c2.forward_packed(b1, bits_out=True)
+        out3 = c3.forward_packed(b2)
+        out2 = c2.forward_packed(b1)
+        torch.cuda.synchronize()
+        b1h, b2h = b1.cpu().numpy(), b2.cpu().numpy()
+        parity.compare_bits(l1, in1, b1h)
+        sub2 = dict(in2, x=parity.values_from_bits(b1h, l2.in_c))
+        ref2 = oracle.bconv_layer(l2, sub2)
+        bound2 = parity.output_bound(l2, sub2, ref2)
+        assert np.all(np.abs(out2.cpu().numpy().astype(np.float64) - ref2["out"]) <= bound2)
+        assert np.array_equal(parity.unpack_words(b2h, l2.out_c), (~(out2.cpu().numpy() < 0)).astype(np.uint8))
+        parity.compare_bits(l2, sub2, b2h, ref=ref2)
+        sub3 = dict(in3, x=parity.values_from_bits(b2h, l3.in_c))
+        ref3 = oracle.bconv_layer(l3, sub3)
+        bound3 = parity.output_bound(l3, sub3, ref3)
+        assert np.all(np.abs(out3.cpu().numpy().astype(np.float64) - ref3["out"]) <= bound3)
+    finally:
+        for c in (c1, c2, c3):
+            c.close()
+
+
+def test_packed_input_unsupported(dev):
+    """Handles that read the full-precision input refuse packed input with
+    BCONV_ERR_UNSUPPORTED, before any check of n or pointers."""
+    base = workloads.Layer("unsup", "xnor", 1, 6, 6, 64, 32, 3, 3, 1, 1, 1, 1)
+    cases = [(base.with_(use_beta=True), False), (base.with_(type="binary_weights"), False),
+             (base.with_(iscale_dist=("uniform", 0.5, 1.5)), False),
+             (base.with_(ibias_dist=("normal", 0.0, 0.2)), False), (base, True), (base.with_(type="and"), True)]
+    for layer, int8 in cases:
+        inputs = workloads.make_inputs(layer, 8800)
+        conv = pca.BinaryConvolution.from_layer(layer, inputs, int8_mfma=int8)
+        try:
+            for n in (1, 0):
+                for bits_out in (False, True):
+                    fn = pca.bconv_forward_packed_bits if bits_out else pca.bconv_forward_packed
+                    with pytest.raises(pca.BconvError) as e:
+                        fn(conv.handle, None, n, None, None, None, 0)
+                    assert e.value.status == pca.BCONV_ERR_UNSUPPORTED, (layer, int8)
+        finally:
+            conv.close()
+    # a supported handle: n == 0 is a no-op, NULL pointers and overlap are argument errors
+    inputs = workloads.make_inputs(base, 8801)
+    conv = pca.BinaryConvolution.from_layer(base, inputs)
+    try:
+        pca.bconv_forward_packed(conv.handle, None, 0, None, None, None, 0)
+        ws = conv.workspace(1, dev)
+        buf = torch.zeros(1 << 16, dtype=torch.int32, device=dev)
+        for args in ((None, buf), (buf, None), (buf, buf[1:])):
+            with pytest.raises(pca.BconvError) as e:
+                pca.bconv_forward_packed(conv.handle, None, 1, args[0], args[1], ws, ws.numel())
+            assert e.value.status == pca.BCONV_ERR_INVALID_ARGUMENT
+        with pytest.raises(pca.BconvError) as e:
+            pca.bconv_forward_packed(conv.handle, None, 1, buf, buf[4096:], ws, 16)
+        assert e.value.status == pca.BCONV_ERR_WORKSPACE
+    finally:
+        conv.close()
+
+
 # ------------------------------------------------------------ robustness
 
 def test_repeat_is_bit_identical(dev):
