@@ -132,10 +132,33 @@ def cpu_baseline(layer, inputs, images: int, repeats: int):
         dt = time.perf_counter() - t
         best = dt if best is None else min(best, dt)
     macs = layer.nominal_macs(images)
-    return {"value": macs / best / 1e9, "unit": "GOPS (bit-MAC/s)" if layer.type != "binary_weights"
-            else "GMAC/s (fp32)", "cores": threads, "kind": "oracle",
+    # one host thread on one image: the per-core rate
+    sub1 = dict(inputs)
+    sub1["x"] = np.ascontiguousarray(inputs["x"][:1])
+    t = time.perf_counter()
+    oracle.bconv_layer(layer, sub1, threads=1, want=("out",))
+    one = time.perf_counter() - t
+    unit = "GOPS (bit-MAC/s)" if layer.type != "binary_weights" else "GMAC/s (fp32)"
+    return {"value": macs / best / 1e9, "unit": unit, "cores": threads, "kind": "oracle",
             "sample": f"{images} of {layer.n} images of {layer.name}, best of {repeats} runs "
-                      f"({best:.3f} s each, {macs} nominal MACs)"}
+                      f"({best:.3f} s each, {macs} nominal MACs)",
+            "per_core": {"value": layer.nominal_macs(1) / one / 1e9, "unit": unit, "cores": 1,
+                         "sample": f"1 image, 1 thread ({one:.3f} s)"},
+            "host": host_cpu(), "build": "gcc -std=c11 -O2 -fopenmp -ffp-contract=off (no intrinsics)"}
+
+
+def host_cpu() -> str:
+    """The host CPU's model name and logical core count."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return f"{model}, {os.cpu_count()} logical cores"
 
 
 def cpu_packed_baseline(layer, inputs, repeats: int):
