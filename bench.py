@@ -15,7 +15,9 @@ HBM.  Prints one JSON line:
              path (BCONV_FLAG_INT8_MFMA), timed the same way, with its own
              roofline against the dense int8 MFMA peak or HBM; and the layer
              with its output written as packed sign bits for a next binary
-             layer (bconv_forward_bits), timed the same way;
+             layer (bconv_forward_bits), timed the same way; and (XNOR / AND
+             without beta or input affine) the layer fed packed sign bits
+             (bconv_forward_packed / _bits: repad + convolution), whole steps;
   calibration   measured ceilings of this GPU: the popcount path's two
              instructions on registers (the library's calibration kernel, T
              bit-MAC/s; the roofline object adds the kernel's fraction of it
@@ -274,6 +276,14 @@ def main():
     if not args.no_bits:
         msb, mainb, outb = time_path(pca, torch, np, conv, n, x, stream, args.warmup, args.steps, bits=True)
         del outb
+    packed_ok = (layer.type != "binary_weights" and not layer.use_beta and layer.iscale_dist is None
+                 and layer.ibias_dist is None and not args.profile_only and not args.no_bits)
+    if packed_ok:
+        words = torch.from_numpy(workloads.make_packed_input(layer, workloads.layer_seed(index) + 77).view(np.int32))
+        words = words.to(dev)
+        msp = {fmt: time_packed(pca, torch, conv, n, words, stream, args.warmup, args.steps, fmt == "bits")
+               for fmt in ("fp32", "bits")}
+        del words
     if args.copy_mib > 0:
         src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -355,6 +365,15 @@ def main():
             "output_bytes": (n * layer.out_h * layer.out_w * ((layer.out_c + 31) // 32) * 4),
             "roofline": {"bound": rb[0], "achieved": round(rb[1], 3), "peak": rb[2], "unit": rb[3],
                          "frac": round(rb[1] / rb[2], 4), "algorithmic_bytes": nbb}}
+    if packed_ok:
+        line.setdefault("comparison", {})["packed_input"] = {
+            "what": "bconv_forward_packed: input given as packed sign bits (a previous binary layer's output), "
+                    "so the step is repad + convolution, without the fp32 pack",
+            "input_bytes": n * layer.in_h * layer.in_w * layer.words * 4,
+            "fp32_output": {"value": round(macs / (msp["fp32"] / 1e3) / 1e9, 3), "unit": line["unit"],
+                            "ms_per_step": round(msp["fp32"], 6)},
+            "bits_output": {"value": round(macs / (msp["bits"] / 1e3) / 1e9, 3), "unit": line["unit"],
+                            "ms_per_step": round(msp["bits"], 6)}}
     if not args.no_calibration:
         cal = calibrate(pca, torch, stream)
         line["calibration"] = cal
@@ -453,6 +472,32 @@ def time_path(pca, torch, np, conv, n, x, stream, warmup, steps, bits=False):
     torch.cuda.synchronize()
     main_ms = float(np.mean([b.elapsed_time(e) for b, e in zip(begins, ends)]))
     return t0.elapsed_time(t1) / steps, main_ms, out
+
+
+def time_packed(pca, torch, conv, n, words, stream, warmup, steps, bits_out):
+    """ms per step of `steps` bconv_forward_packed (or _bits) calls on packed
+    input words, between two stream events, after `warmup` untimed calls."""
+    dev = words.device
+    if bits_out:
+        out = torch.empty((n, conv.out_h, conv.out_w, (conv.out_c + 31) // 32), dtype=torch.int32, device=dev)
+        fwd = pca.bconv_forward_packed_bits
+    else:
+        out = torch.empty((n, conv.out_h, conv.out_w, conv.out_c), dtype=torch.float32, device=dev)
+        fwd = pca.bconv_forward_packed
+    ws_bytes = max(1, conv.workspace_bytes(n))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    sptr = stream.cuda_stream
+    for _ in range(warmup):
+        fwd(conv.handle, sptr, n, words, out, ws, ws_bytes)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        fwd(conv.handle, sptr, n, words, out, ws, ws_bytes)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
 
 
 # the source file that defines (and launches) each main kernel, by name prefix
