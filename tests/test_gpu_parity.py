@@ -743,6 +743,20 @@ def test_maximum_sizes(dev, layer):
     parity.compare(layer, inputs, got)
 
 
+MAX_PACKED = [l for l in MAX_CASES if l.type != "binary_weights" and not l.use_beta]
+
+
+@pytest.mark.parametrize("layer", MAX_PACKED, ids=[l.name for l in MAX_PACKED])
+def test_maximum_sizes_packed(dev, layer):
+    """Packed sign-bit input at the largest window and image extent."""
+    seed = 4450 + MAX_PACKED.index(layer)
+    inputs = workloads.make_inputs(layer, seed)
+    words = workloads.make_packed_input(layer, seed + 1)
+    _log(f"max packed {layer.name}")
+    r = _packed_run(layer, inputs, words, dev)
+    _check_packed(layer, inputs, words, r)
+
+
 def test_maximum_window_is_exact(dev):
     """All 2^24 products of the largest window agree: the XNOR and AND sums
     reach exactly 2^24 (the top of the exact fp32 integers) and the output is
