@@ -220,7 +220,11 @@ bconv_status_t bconv_workspace_layout(bconv_t h, int32_t n, bconv_workspace_layo
  * caller and must stay valid until the stream work completes; `in` and `out`
  * must not overlap.  n == 0 is a no-op.  Never allocates and never
  * synchronises.  One handle may serve several streams at once when each call
- * has its own workspace. */
+ * has its own workspace.  Errors: INVALID_ARGUMENT for a NULL handle or
+ * pointer, n < 0, overlapping buffers, or a batch too large for one call
+ * (n*H*W >= 2^31, input or output of 2 GiB or more, n*Ho*Wo*ceil(Cout/64)
+ * >= 2^29, or a padded bit buffer of 2^31 words or more); WORKSPACE for a
+ * missing or short workspace; HIP when a launch fails. */
 bconv_status_t bconv_forward(bconv_t h, void *stream, int32_t n, const float *in, float *out,
                              void *workspace, size_t workspace_bytes);
 

@@ -256,6 +256,10 @@ bconv_status_t forward_impl(bconv_t h, void *stream, int32_t n, const void *src,
         return fail(BCONV_ERR_INVALID_ARGUMENT,
                     "batch too large for one call: input and output must each stay below 2 GiB");
     const bconv_workspace_layout_t L = layout_for(h, n);
+    if (L.bits_offset != SIZE_MAX && (long long)n * L.bits_rows * L.bits_cols * L.bits_words +
+                                             make_geom(h, n).bits_slack_words >= 0x7fffffffLL)
+        return fail(BCONV_ERR_INVALID_ARGUMENT,
+                    "batch too large for one call: the padded bit buffer must stay below 2^31 words");
     if (L.total_bytes > 0 && (!workspace || workspace_bytes < L.total_bytes))
         return fail(BCONV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total_bytes,
                     workspace ? workspace_bytes : (size_t)0);

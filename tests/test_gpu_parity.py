@@ -609,6 +609,24 @@ def test_packed_chain(dev):
             c.close()
 
 
+def test_packed_batch_limit(dev):
+    """A batch whose padded bit buffer would reach 2^31 words is an argument
+    error, found before any launch (a 1x1 image has 9 padded pixels under a
+    3x3 window; input and output stay below 2 GiB).  The pointers are never
+    dereferenced: without this check the missing workspace is the error."""
+    layer = workloads.Layer("tiny_image", "xnor", 1, 1, 1, 32, 1, 3, 3, 1, 1, 1, 1)
+    conv = pca.BinaryConvolution.from_layer(layer, workloads.make_inputs(layer, 8802))
+    try:
+        n = (1 << 31) // 9 + 1
+        for fn in (pca.bconv_forward_packed, pca.bconv_forward_packed_bits):
+            with pytest.raises(pca.BconvError) as e:
+                fn(conv.handle, None, n, 0x10000000000, 0x20000000000, None, 0)
+            assert e.value.status == pca.BCONV_ERR_INVALID_ARGUMENT, pca.bconv_last_error()
+            assert "2^31 words" in pca.bconv_last_error()
+    finally:
+        conv.close()
+
+
 def test_packed_input_unsupported(dev):
     """Handles that read the full-precision input refuse packed input with
     BCONV_ERR_UNSUPPORTED, before any check of n or pointers."""
