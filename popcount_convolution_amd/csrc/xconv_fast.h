@@ -331,14 +331,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void x
     const uint32_t coff = co_ok ? (uint32_t)(co * 4) : 0x80000000u;
     auto emit = [&](auto full) {
         if (a.bits_out) {
+            // one unrolled loop per activation class, as for the values below
+            auto store_bits_all = [&](auto bit_of) {
 #pragma unroll
-            for (int p = 0; p < P; ++p) {
-                const int ox = ow0 + p;
-                if (ox >= a.out_w) break;
-                const float be = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(be_lane), p));
-                store_tile_bits(a.bits_out, ((long long)img * a.out_h + oy) * a.out_w + ox, a.out_words, (int)tile,
-                                co_ok && sign_bit(epilogue_value((float)window_value(full, p, ox), sc, be, bi, a.neuron)));
-            }
+                for (int p = 0; p < P; ++p) {
+                    const int ox = ow0 + p;
+                    if (ox >= a.out_w) break;
+                    const float be = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(be_lane), p));
+                    store_tile_bits(a.bits_out, ((long long)img * a.out_h + oy) * a.out_w + ox, a.out_words,
+                                    (int)tile, co_ok && bit_of(window_value(full, p, ox), be));
+                }
+            };
+            if (a.neuron.type == kNeuronRelu)
+                store_bits_all([](int, float) { return true; });  // a ReLU output is never below 0
+            else if (a.neuron.type == kNeuronNone)
+                store_bits_all([&](int v, float be) { return sign_bit(__builtin_fmaf((float)v * sc, be, bi)); });
+            else
+                store_bits_all(
+                    [&](int v, float be) { return sign_bit(epilogue_value((float)v, sc, be, bi, a.neuron)); });
             return;
         }
         // One unrolled loop per output form (window sums, values with and
