@@ -326,6 +326,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void x
             return a.in_c * valid - 2 * ((int)acc[p] - corr);
         }
     };
+    // The same value as a float, exactly (|value| < 2^24): the full-window
+    // XNOR form is one fma on the converted count.
+    auto window_value_f = [&](auto full, int p, int ox) -> float {
+        if constexpr (!AND && decltype(full)::value)
+            return __builtin_fmaf((float)acc[p], -2.0f, (float)full_taps);
+        else
+            return (float)window_value(full, p, ox);
+    };
     // Lanes past out_c store at an out-of-range offset, which the buffer range
     // check discards.
     const uint32_t coff = co_ok ? (uint32_t)(co * 4) : 0x80000000u;
@@ -339,16 +347,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void x
                     if (ox >= a.out_w) break;
                     const float be = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(be_lane), p));
                     store_tile_bits(a.bits_out, ((long long)img * a.out_h + oy) * a.out_w + ox, a.out_words,
-                                    (int)tile, co_ok && bit_of(window_value(full, p, ox), be));
+                                    (int)tile, co_ok && bit_of(p, ox, be));
                 }
             };
             if (a.neuron.type == kNeuronRelu)
-                store_bits_all([](int, float) { return true; });  // a ReLU output is never below 0
+                store_bits_all([](int, int, float) { return true; });  // a ReLU output is never below 0
             else if (a.neuron.type == kNeuronNone)
-                store_bits_all([&](int v, float be) { return sign_bit(__builtin_fmaf((float)v * sc, be, bi)); });
+                store_bits_all([&](int p, int ox, float be) {
+                    return sign_bit(__builtin_fmaf(window_value_f(full, p, ox) * sc, be, bi));
+                });
             else
-                store_bits_all(
-                    [&](int v, float be) { return sign_bit(epilogue_value((float)v, sc, be, bi, a.neuron)); });
+                store_bits_all([&](int p, int ox, float be) {
+                    return sign_bit(epilogue_value(window_value_f(full, p, ox), sc, be, bi, a.neuron));
+                });
             return;
         }
         // One unrolled loop per output form (window sums, values with and
@@ -359,23 +370,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void x
                 const int ox = ow0 + p;
                 if (ox >= a.out_w) break;
                 const float be = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(be_lane), p));
-                __builtin_amdgcn_raw_buffer_store_b32(value_bits(window_value(full, p, ox), be), orr, coff,
+                __builtin_amdgcn_raw_buffer_store_b32(value_bits(p, ox, be), orr, coff,
                                                       __builtin_amdgcn_readfirstlane(obase + (uint32_t)p * ostep),
                                                       kStoreSc1);
             }
         };
         if (a.acc_out)
-            store_all([](int v, float) { return (uint32_t)v; });
+            store_all([&](int p, int ox, float) { return (uint32_t)window_value(full, p, ox); });
         else if (a.neuron.type == kNeuronRelu)
-            store_all([&](int v, float be) {
-                const float r = __builtin_fmaf((float)v * sc, be, bi);
+            store_all([&](int p, int ox, float be) {
+                const float r = __builtin_fmaf(window_value_f(full, p, ox) * sc, be, bi);
                 return __builtin_bit_cast(uint32_t, (r < 0.0f) ? 0.0f : r);
             });
         else if (a.neuron.type == kNeuronNone)
-            store_all([&](int v, float be) { return __builtin_bit_cast(uint32_t, __builtin_fmaf((float)v * sc, be, bi)); });
+            store_all([&](int p, int ox, float be) {
+                return __builtin_bit_cast(uint32_t, __builtin_fmaf(window_value_f(full, p, ox) * sc, be, bi));
+            });
         else
-            store_all([&](int v, float be) {
-                return __builtin_bit_cast(uint32_t, epilogue_value((float)v, sc, be, bi, a.neuron));
+            store_all([&](int p, int ox, float be) {
+                return __builtin_bit_cast(uint32_t, epilogue_value(window_value_f(full, p, ox), sc, be, bi, a.neuron));
             });
     };
     if (!AND && border)
