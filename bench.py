@@ -64,7 +64,7 @@ def algorithmic_bytes(layer, n, bits_out=False):
     if layer.is_fc:
         rows, cols = layer.in_h, layer.in_w
     else:
-        rows, cols = layer.in_h + 2 * layer.pad_h, layer.in_w + 2 * layer.pad_w
+        rows, cols = layer.in_h + layer.pad_h + layer.pad_h_end, layer.in_w + layer.pad_w + layer.pad_w_end
     if layer.type == "binary_weights":
         src = n * layer.in_h * layer.in_w * layer.in_c * 4
     else:
@@ -83,7 +83,7 @@ def int8_algorithmic_bytes(layer, n):
     if layer.is_fc:
         rows, cols = layer.in_h, layer.in_w
     else:
-        rows, cols = layer.in_h + 2 * layer.pad_h, layer.in_w + 2 * layer.pad_w
+        rows, cols = layer.in_h + layer.pad_h + layer.pad_h_end, layer.in_w + layer.pad_w + layer.pad_w_end
     src = n * rows * cols * cpad
     amap = n * rows * cols * 4 if layer.use_beta else 0
     weights = layer.out_c * layer.kernel_h * layer.kernel_w * cpad
@@ -241,8 +241,8 @@ def run_sweep(args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not offered (every box here has "
-              "one MI355X). Run with --gpus 1.", file=sys.stderr)
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not offered, the path runs on a single "
+              "MI355X and has no multi-GPU form. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
