@@ -715,6 +715,57 @@ def test_new_input_reuses_workspace(dev, layer):
         conv.close()
 
 
+def test_graph_capture_replays(dev):
+    """The forward entry points only launch kernels (no allocation, memset or
+    synchronisation inside), so a chain of them records into a HIP graph:
+    fp32 output, packed sign bits, and a next layer fed those bits.  Every
+    replay, after the outputs and workspaces are poisoned eagerly between
+    replays, gives the eager results bit for bit."""
+    l1 = workloads.BENCH_LAYER.with_(n=2)
+    l2 = workloads.Layer("graph_and_s2", "and", 2, 56, 56, 128, 64, 3, 3, 2, 2, 1, 1)
+    in1, in2 = workloads.make_inputs(l1, 8900), workloads.make_inputs(l2, 8901)
+    c1, c2 = pca.BinaryConvolution.from_layer(l1, in1), pca.BinaryConvolution.from_layer(l2, in2)
+    try:
+        x = torch.from_numpy(in1["x"]).to(dev)
+        ws1, ws2 = c1.workspace(2, dev), c2.workspace(2, dev)
+        out1 = torch.empty((2, c1.out_h, c1.out_w, c1.out_c), dtype=torch.float32, device=dev)
+        bits1 = torch.empty((2, c1.out_h, c1.out_w, c1.out_words()), dtype=torch.int32, device=dev)
+        out2 = torch.empty((2, c2.out_h, c2.out_w, c2.out_c), dtype=torch.float32, device=dev)
+
+        def chain():
+            c1.forward(x, out1, ws1)
+            c1.forward_bits(x, bits1, ws1)
+            c2.forward_packed(bits1, out2, ws2)
+
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            chain()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        want = [t.clone() for t in (out1, bits1, out2)]
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            chain()
+        torch.cuda.synchronize()
+        for replay in range(3):
+            out1.fill_(float("nan"))
+            bits1.fill_(-1)
+            out2.fill_(float("nan"))
+            ws1.fill_(0xA5)
+            ws2.fill_(0x5A)
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            _log(f"graph replay {replay}")
+            for got, ref in zip((out1, bits1, out2), want):
+                assert torch.equal(got.view(torch.int32), ref.view(torch.int32)), f"replay {replay} differs"
+        del graph
+    finally:
+        c1.close()
+        c2.close()
+
+
 def test_two_streams_share_a_handle(dev):
     layer = workloads.LAYERS[2].with_(n=4)
     inputs = workloads.make_inputs(layer, 4)
