@@ -11,8 +11,9 @@
 // followed by the fused epilogue  neuron(v*scale[c]*beta + bias[c]).
 //
 // Mapping on gfx950: a wave owns 64 output channels (one per lane) of a
-// strip of P neighbouring output pixels.  Kernel rows are walked in order;
-// for each, every lane loads its channel's weight words of that row into
+// strip of P neighbouring output pixels.  The kernel rows inside the image
+// are walked in order (rows in the padding contribute nothing and are
+// skipped); for each, every lane loads its channel's weight words of that row into
 // VGPRs (16-byte loads from an L1/L2-resident table), and the binarised input
 // words of the strip, the same for every lane, are fetched with scalar loads
 // into SGPRs and fed to v_xor_b32 / v_and_b32 as the scalar operand;
@@ -199,36 +200,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void x
     const int iy0 = oy * a.sh - a.ph;
     const int r0 = iy0 < 0 ? -iy0 : 0;
     const int r1 = a.in_h - iy0 < KH ? a.in_h - iy0 : KH;
-    // XNOR border correction: a zero input word at a padded tap counts every
-    // set weight bit as a disagreement; those bits are total - (in-image
-    // rectangle), from the lane's prefix sums rect[a][b] (taps ky < a, kx < b).
-    // A strip needs rows r0 and r1 of the table and the total.
-    // (read only on border strips, where they are loaded below)
-    int rt0[KW + 1], rt1[KW + 1], rtotal;
+    // Kernel rows outside the image are skipped.  XNOR border correction for
+    // the padded columns of the rows that remain: a zero input word at a
+    // padded tap counts every set weight bit as a disagreement; those bits
+    // are (rows r0..r1, all columns) - (in-image rectangle), from the lane's
+    // prefix sums rect[a][b] (taps ky < a, kx < b), rows r0 and r1 of the
+    // table.  (read only on border strips, where they are loaded below)
+    int rt0[KW + 1], rt1[KW + 1];
     const int ixa = ow0 * SW - a.pw;                 // first pixel's first tap column
     const int ixz = (ow0 + P - 1) * SW - a.pw + KW;  // one past the last pixel's last tap
     const bool border = r0 > 0 || r1 < KH || ixa < 0 || ixz > a.in_w;
     if (!AND && border) {
-        // lane-major table: this lane's rows r0, r1 and KH are whole 16-byte loads
+        // lane-major table: this lane's rows r0 and r1 are whole 16-byte loads
         constexpr int RR = (KW + 1 + 3) / 4 * 4;
         const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.wrect, a.wrect_bytes);
         const uint32_t lbase = (uint32_t)((tile * 64 + lane) * (KH + 1) * RR) * 4u;
-        int t0[RR], t1[RR], tk[RR];
+        int t0[RR], t1[RR];
 #pragma unroll
         for (int q = 0; q < RR / 4; ++q) {
             const uint4 v0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rr, lbase, (r0 * RR + 4 * q) * 4, 0));
             const uint4 v1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rr, lbase, (r1 * RR + 4 * q) * 4, 0));
-            const uint4 vk = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rr, lbase, (KH * RR + 4 * q) * 4, 0));
             t0[4 * q] = (int)v0.x; t0[4 * q + 1] = (int)v0.y; t0[4 * q + 2] = (int)v0.z; t0[4 * q + 3] = (int)v0.w;
             t1[4 * q] = (int)v1.x; t1[4 * q + 1] = (int)v1.y; t1[4 * q + 2] = (int)v1.z; t1[4 * q + 3] = (int)v1.w;
-            tk[4 * q] = (int)vk.x; tk[4 * q + 1] = (int)vk.y; tk[4 * q + 2] = (int)vk.z; tk[4 * q + 3] = (int)vk.w;
         }
 #pragma unroll
         for (int c = 0; c <= KW; ++c) {
             rt0[c] = t0[c];
             rt1[c] = t1[c];
         }
-        rtotal = tk[KW];
     }
 
     uint32_t acc[P];
@@ -238,12 +237,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void x
     const scalar_u32_ptr bits = (scalar_u32_ptr)a.bits;
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.wlane, a.wlane_bytes);
     const uint32_t wbase = tile * (uint32_t)(KH * RW4 * 1024);
-    // Kernel rows stay a rolled loop: the strip words are invariant loads, and
-    // an unrolled row loop lets the compiler hoist every row's scalar loads
-    // at once, which overflows the SGPR file.  The row's weights (RW words)
-    // are re-read from the L1/L2-resident table each row.
+    // Kernel rows stay a rolled loop over the strip's in-image rows: the strip
+    // words are invariant loads, and an unrolled row loop lets the compiler
+    // hoist every row's scalar loads at once, which overflows the SGPR file.
+    // The row's weights (RW words) are re-read from the L1/L2-resident table
+    // each row.
 #pragma unroll 1
-    for (int ky = 0; ky < KH; ++ky) {
+    for (int ky = r0; ky < r1; ++ky) {
         uint32_t w[RW4 * 4];
 #pragma unroll
         for (int q = 0; q < RW4; ++q) {
@@ -313,15 +313,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void x
             const int valid = (r1 - r0) * (c1 - c0);
             int corr = 0;
             if (valid != KH * KW) {
-                // set weight bits at padded taps = total - in-image rectangle
-                // (c0, c1 are wave-uniform: a select chain, no register indexing)
+                // set weight bits at the padded taps of the rows taken =
+                // row band - in-image rectangle (c0, c1 are wave-uniform: a
+                // select chain, no register indexing)
                 int a0 = 0, a1 = 0, b0 = 0, b1 = 0;
 #pragma unroll
                 for (int c = 0; c <= KW; ++c) {
                     if (c == c0) { a0 = rt0[c]; a1 = rt1[c]; }
                     if (c == c1) { b0 = rt0[c]; b1 = rt1[c]; }
                 }
-                corr = rtotal - (b1 - b0 - a1 + a0);
+                corr = (rt1[KW] - rt0[KW]) - (b1 - b0 - a1 + a0);
             }
             return a.in_c * valid - 2 * ((int)acc[p] - corr);
         }
