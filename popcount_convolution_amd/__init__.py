@@ -28,6 +28,42 @@ from ._binding import (  # noqa: F401  (re-exported C ABI names)
     bconv_workspace_size, load_library, make_desc)
 
 
+def check_tensor(t, name: str, shape, dtypes, device=None) -> None:
+    """Raise ValueError unless ``t`` is a contiguous CUDA tensor of exactly
+    ``shape`` with one of ``dtypes`` (on ``device`` when given).  The C entry
+    points size every buffer from the layer descriptor, so a tensor that is
+    smaller, strided or of another element type would be read or written
+    past its end, or misread."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name}: a torch tensor is required, got {type(t).__name__}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name}: dtype {t.dtype} is not one of {', '.join(str(d) for d in dtypes)}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)} != {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: the tensor must be contiguous (NHWC, dense)")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: a CUDA (HIP) device tensor is required, got device {t.device}")
+    if device is not None and t.device != torch.device(device):
+        raise ValueError(f"{name}: on {t.device}, the input is on {device}")
+
+
+def check_workspace(ws, need: int, device) -> None:
+    """Raise ValueError unless ``ws`` is a contiguous device tensor on
+    ``device`` holding at least ``need`` bytes."""
+    import torch
+    if not isinstance(ws, torch.Tensor):
+        raise ValueError(f"workspace: a torch tensor is required, got {type(ws).__name__}")
+    if not ws.is_contiguous():
+        raise ValueError("workspace: the tensor must be contiguous")
+    if ws.device.type != "cuda" or ws.device != torch.device(device):
+        raise ValueError(f"workspace: on {ws.device}, the input is on {device}")
+    have = ws.numel() * ws.element_size()
+    if have < need:
+        raise ValueError(f"workspace: {have} bytes given, {need} needed")
+
+
 class BinaryConvolution:
     """One binary convolution layer on the current GPU.
 
@@ -53,6 +89,7 @@ class BinaryConvolution:
             (BCONV_FLAG_BETA_VALID_TAPS if beta_valid_taps else BCONV_FLAG_NONE)
         self.handle = bconv_create(self.desc, weight_bits, output_scale, output_bias,
                                    input_scale, input_bias, self.type, self.flags)
+        self.in_h, self.in_w = in_h, in_w
         self.in_c, self.out_c, self.out_h, self.out_w = bconv_get_info(self.handle)
 
     @classmethod
@@ -77,66 +114,70 @@ class BinaryConvolution:
         return torch.empty(max(1, self.workspace_bytes(n)), dtype=torch.uint8,
                            device=device or "cuda")
 
-    def _stream(self, stream):
+    def out_words(self) -> int:
+        return (self.out_c + 31) // 32
+
+    def in_words(self) -> int:
+        return (self.in_c + 31) // 32
+
+    def _launch(self, fn, x, x_shape, x_dtypes, out, out_shape, out_dtype, workspace, stream):
+        """Checks the tensors against the layer, allocates what the caller did
+        not pass on the launch stream itself (so the caching allocator never
+        hands those blocks to other work while the kernels still use them),
+        then calls the C entry point ``fn``."""
         import torch
-        return (stream or torch.cuda.current_stream()).cuda_stream
+        n = x.shape[0] if isinstance(x, torch.Tensor) and x.dim() == 4 else -1
+        check_tensor(x, "input", x_shape(n), x_dtypes)
+        s = stream or torch.cuda.current_stream(x.device)
+        with torch.cuda.device(x.device), torch.cuda.stream(s):
+            if out is None:
+                out = torch.empty(out_shape(n), dtype=out_dtype, device=x.device)
+            if workspace is None:
+                workspace = self.workspace(n, x.device)
+        check_tensor(out, "output", out_shape(n), (out_dtype,), device=x.device)
+        check_workspace(workspace, self.workspace_bytes(n), x.device)
+        fn(self.handle, s.cuda_stream, n, x, out, workspace, workspace.numel() * workspace.element_size())
+        return out
+
+    def _in_shape(self, n):
+        return (n, self.in_h, self.in_w, self.in_c)
+
+    def _out_shape(self, n):
+        return (n, self.out_h, self.out_w, self.out_c)
+
+    def _bits_shape(self, n):
+        return (n, self.out_h, self.out_w, self.out_words())
 
     def forward(self, x, out=None, workspace=None, stream=None):
+        """float32 NHWC input [n, in_h, in_w, in_c] -> float32 NHWC output."""
         import torch
-        n = x.shape[0]
-        if out is None:
-            out = torch.empty((n, self.out_h, self.out_w, self.out_c), dtype=torch.float32,
-                              device=x.device)
-        if workspace is None:
-            workspace = self.workspace(n, x.device)
-        bconv_forward(self.handle, self._stream(stream), n, x, out, workspace,
-                      workspace.numel() * workspace.element_size())
-        return out
+        return self._launch(bconv_forward, x, self._in_shape, (torch.float32,), out, self._out_shape,
+                            torch.float32, workspace, stream)
 
     def forward_accum(self, x, acc=None, workspace=None, stream=None):
         """Window sums before the epilogue: int32 (XNOR/AND) or float32."""
         import torch
-        n = x.shape[0]
-        if acc is None:
-            dt = torch.float32 if self.type == BCONV_BINARY_WEIGHTS else torch.int32
-            acc = torch.empty((n, self.out_h, self.out_w, self.out_c), dtype=dt, device=x.device)
-        if workspace is None:
-            workspace = self.workspace(n, x.device)
-        bconv_forward_accum(self.handle, self._stream(stream), n, x, acc, workspace,
-                            workspace.numel() * workspace.element_size())
-        return acc
-
-    def out_words(self) -> int:
-        return (self.out_c + 31) // 32
+        dt = torch.float32 if self.type == BCONV_BINARY_WEIGHTS else torch.int32
+        return self._launch(bconv_forward_accum, x, self._in_shape, (torch.float32,), acc, self._out_shape, dt,
+                            workspace, stream)
 
     def forward_bits(self, x, out_bits=None, workspace=None, stream=None):
         """Packed sign bits of the output (see bconv_forward_bits), as int32
         words [n, out_h, out_w, ceil(out_c/32)] holding the uint32 bit patterns."""
         import torch
-        n = x.shape[0]
-        if out_bits is None:
-            out_bits = torch.empty((n, self.out_h, self.out_w, self.out_words()), dtype=torch.int32,
-                                   device=x.device)
-        if workspace is None:
-            workspace = self.workspace(n, x.device)
-        bconv_forward_bits(self.handle, self._stream(stream), n, x, out_bits, workspace,
-                           workspace.numel() * workspace.element_size())
-        return out_bits
+        return self._launch(bconv_forward_bits, x, self._in_shape, (torch.float32,), out_bits, self._bits_shape,
+                            torch.int32, workspace, stream)
 
     def forward_packed(self, x_bits, out=None, workspace=None, stream=None, bits_out=False):
         """Forward pass from packed input sign bits (see bconv_forward_packed):
         int32 words [n, in_h, in_w, ceil(in_c/32)], e.g. a previous layer's
         forward_bits.  Returns fp32 NHWC, or packed output bits with bits_out."""
         import torch
-        n = x_bits.shape[0]
-        if out is None:
-            shape = (n, self.out_h, self.out_w, self.out_words() if bits_out else self.out_c)
-            out = torch.empty(shape, dtype=torch.int32 if bits_out else torch.float32, device=x_bits.device)
-        if workspace is None:
-            workspace = self.workspace(n, x_bits.device)
         fn = bconv_forward_packed_bits if bits_out else bconv_forward_packed
-        fn(self.handle, self._stream(stream), n, x_bits, out, workspace, workspace.numel() * workspace.element_size())
-        return out
+        return self._launch(fn, x_bits, lambda n: (n, self.in_h, self.in_w, self.in_words()),
+                            (torch.int32, torch.uint32) if hasattr(torch, "uint32") else (torch.int32,),
+                            out, self._bits_shape if bits_out else self._out_shape,
+                            torch.int32 if bits_out else torch.float32, workspace, stream)
 
     def main_kernel(self, n: int) -> str:
         return bconv_main_kernel(self.handle, n)

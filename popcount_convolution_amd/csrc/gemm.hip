@@ -104,6 +104,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void b
     for (int q = qfull > q0 ? qfull : q0; q < q1; ++q) {
         const uint4 wv = wl[(long long)q * 64];
         const uint32_t w[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
         for (int r = 0; r < kMR; ++r) {
             const int rr = r < rows_valid ? r : rows_valid - 1;
 #pragma unroll

@@ -6,13 +6,14 @@
 //   AND:  popcount(x & w) per word.
 // followed by the fused epilogue  neuron(v*scale[c]*beta + bias[c]).
 //
-// Mapping on gfx950: a wave owns 64 output channels (one per lane).  Each
-// lane keeps its channel's whole weight window in VGPRs.  The binarised
-// input words of a strip of P neighbouring output pixels are the same for
-// every lane, so they are fetched with scalar loads into SGPRs and fed to
-// v_xor_b32 / v_and_b32 as the scalar operand; v_bcnt_u32_b32 then counts and
-// accumulates in one instruction.  Two VALU instructions per word pair, no LDS
-// and no vector loads in the inner loop.
+// Mapping on gfx950: a wave owns 64 output channels (one per lane).  The
+// binarised input words under the window are the same for every lane, so they
+// are fetched with scalar loads into SGPRs and fed to v_xor_b32 / v_and_b32 as
+// the scalar operand; v_bcnt_u32_b32 then counts and accumulates in one
+// instruction, two VALU instructions per word pair.  A lane's weight words come
+// from the lane-major table (256 contiguous bytes per wave per 4 words): the
+// specialised kernel reads them once per kernel row for a whole strip of output
+// pixels, the generic kernel below once per tap for its single pixel.  No LDS.
 //
 // The specialised kernel (xconv_fast.h) is compiled per shape in
 // xconv_k*.hip; this file holds the kernel for any geometry and the dispatch.

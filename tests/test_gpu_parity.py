@@ -31,19 +31,33 @@ def _log(msg):
 
 # ------------------------------------------------------------ measured layers
 
+_MEASURED_REF = {}
+
+
+def measured_reference(index):
+    """Seeded inputs of measured layer ``index`` and the oracle's result on the
+    whole batch (computed once per test session: the fp32, int8 and sign-bit
+    tests of a layer compare against the same reference)."""
+    if index not in _MEASURED_REF:
+        layer = workloads.LAYERS[index]
+        inputs = workloads.make_inputs(layer, workloads.layer_seed(index))
+        _MEASURED_REF.clear()  # one layer's reference at a time bounds host memory
+        _MEASURED_REF[index] = (inputs, oracle.bconv_layer(layer, inputs))
+    return _MEASURED_REF[index]
+
+
 @pytest.mark.parametrize("index", range(len(workloads.LAYERS)),
                          ids=[l.name for l in workloads.LAYERS])
-def test_measured_layer_sampled(dev, index):
+def test_measured_layer_full(dev, index):
     """Each measured layer at full size, in the launch configuration the
-    benchmark times; the oracle checks the first and last images (all of a
-    single-image layer), FC rows 0, 1 and the last."""
+    benchmark times, compared with the oracle on every output of the whole
+    batch (every image, so every XCD's share of the strips, and every row
+    group of the fully connected product)."""
     layer = workloads.LAYERS[index]
-    inputs = workloads.make_inputs(layer, workloads.layer_seed(index))
     _log(f"layer {layer.name} seed {workloads.layer_seed(index)}")
+    inputs, ref = measured_reference(index)
     got = parity.run_gpu(layer, inputs, dev)
-    n = layer.n
-    images = sorted({0, 1, n - 1}) if layer.is_fc else sorted({0, n - 1})
-    parity.compare(layer, inputs, got, images=np.array(images))
+    parity.compare(layer, inputs, got, ref=ref)
 
 
 def test_small_layer_full(dev):
@@ -371,17 +385,15 @@ INT8_MEASURED = [i for i, l in enumerate(workloads.LAYERS) if l.type != "binary_
 
 
 @pytest.mark.parametrize("index", INT8_MEASURED, ids=[workloads.LAYERS[i].name for i in INT8_MEASURED])
-def test_int8_mfma_measured_layer_sampled(dev, index):
-    """The int8 path on each XNOR / AND measured layer at full size, sampled
-    as in the popcount path's measured-layer test."""
+def test_int8_mfma_measured_layer_full(dev, index):
+    """The int8 path on each XNOR / AND measured layer at full size, every
+    output compared with the oracle."""
     layer = workloads.LAYERS[index]
-    inputs = workloads.make_inputs(layer, workloads.layer_seed(index))
     _log(f"int8 layer {layer.name} seed {workloads.layer_seed(index)}")
+    inputs, ref = measured_reference(index)
     got = parity.run_gpu(layer, inputs, dev, int8_mfma=True)
     assert got["main_kernel"] == "i8mma_kernel"
-    n = layer.n
-    images = sorted({0, 1, n - 1}) if layer.is_fc else sorted({0, n - 1})
-    parity.compare(layer, inputs, got, images=np.array(images))
+    parity.compare(layer, inputs, got, ref=ref)
 
 
 @pytest.mark.parametrize("layer", INT8_LAYERS, ids=[l.name for l in INT8_LAYERS])
@@ -453,16 +465,15 @@ def test_forward_bits(dev, layer):
 
 @pytest.mark.parametrize("index", range(len(workloads.LAYERS)), ids=[l.name for l in workloads.LAYERS])
 def test_forward_bits_measured_layer(dev, index):
-    """Sign bits on each measured layer at full size (oracle on sampled images)."""
+    """Sign bits on each measured layer at full size, every bit compared with
+    the oracle's signs (where fp32 rounding cannot decide them)."""
     layer = workloads.LAYERS[index]
-    inputs = workloads.make_inputs(layer, workloads.layer_seed(index))
     _log(f"bits layer {layer.name}")
+    inputs, ref = measured_reference(index)
     words, out, kernel = _run_bits(layer, inputs, dev)
     bits = parity.unpack_words(words, layer.out_c)
     assert np.array_equal(bits, (~(out < 0)).astype(np.uint8)), f"{kernel}: bits differ from its fp32 signs"
-    n = layer.n
-    images = sorted({0, 1, n - 1}) if layer.is_fc else sorted({0, n - 1})
-    parity.compare_bits(layer, inputs, words, images=np.array(images))
+    parity.compare_bits(layer, inputs, words, ref=ref)
 
 
 # ------------------------------------------------ packed sign-bit input
@@ -563,15 +574,14 @@ PACKED_MEASURED = [i for i, l in enumerate(workloads.LAYERS)
 
 @pytest.mark.parametrize("index", PACKED_MEASURED, ids=[workloads.LAYERS[i].name for i in PACKED_MEASURED])
 def test_forward_packed_measured_layer(dev, index):
-    """Packed input on each measured layer it applies to, at full size (oracle
-    on sampled images)."""
+    """Packed input on each measured layer it applies to, at full size, every
+    output compared with the oracle on the +-1 input the words stand for."""
     layer = workloads.LAYERS[index]
     inputs = workloads.make_inputs(layer, workloads.layer_seed(index))
     words = workloads.make_packed_input(layer, workloads.layer_seed(index) + 77)
     _log(f"packed layer {layer.name}")
     r = _packed_run(layer, inputs, words, dev)
-    n = layer.n
-    _check_packed(layer, inputs, words, r, images=np.array(sorted({0, n // 2, n - 1})))
+    _check_packed(layer, inputs, words, r)
 
 
 def test_packed_chain(dev):
@@ -785,6 +795,39 @@ def test_two_streams_share_a_handle(dev):
         conv.close()
 
 
+def test_temporaries_on_a_side_stream(dev):
+    """forward*(stream=s) with s not the current stream and no workspace or
+    output given: the wrapper allocates them on s, so blocks the current
+    stream allocates and overwrites right after the launch are never the ones
+    the kernels still use.  Every call matches the oracle."""
+    layer = workloads.BENCH_LAYER.with_(n=4)
+    inputs = workloads.make_inputs(layer, 31)
+    ref = oracle.bconv_layer(layer, inputs)
+    conv = pca.BinaryConvolution.from_layer(layer, inputs)
+    try:
+        x = torch.from_numpy(inputs["x"]).to(dev)
+        side = torch.cuda.Stream()
+        nbytes = conv.workspace_bytes(4)
+        torch.cuda.synchronize()
+        side.wait_stream(torch.cuda.current_stream())
+        outs, accs = [], []
+        for _ in range(4):
+            outs.append(conv.forward(x, stream=side))
+            accs.append(conv.forward_accum(x, stream=side))
+            # allocations of the freed temporaries' sizes on the current
+            # stream, overwritten at once
+            for _ in range(3):
+                torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(0x5A)
+                torch.empty(outs[-1].shape, dtype=torch.float32, device=dev).fill_(float("nan"))
+        side.synchronize()
+        torch.cuda.synchronize()
+        for out, acc in zip(outs, accs):
+            parity.compare(layer, inputs, {"out": out.cpu().numpy(), "acc": acc.cpu().numpy()}, ref=ref,
+                           workspace=False)
+    finally:
+        conv.close()
+
+
 # ------------------------------------------------------------ maximum sizes
 
 MAX_CHANNELS = 1 << 20   # the C ABI's in_c limit
@@ -909,3 +952,68 @@ def test_fc_entry_point_matches_conv(dev):
     finally:
         pca.bconv_destroy(h)
         conv.close()
+
+
+# ------------------------------------- FC shapes whose window is not 4k words
+
+def _fc_tail_layers():
+    """Fully connected shapes (kernel = source size, MPSCNNFullyConnected
+    conditions) whose K = kh*kw*ceil(in_c/32) words leave 1, 2 or 3 words in
+    the matrix kernel's last 4-word step, at batches that are not a multiple of
+    its 16-row groups; XNOR and AND, plain and with beta + input affine."""
+    base = workloads.Layer("fc_tail", "xnor", 17, 1, 1, 64, 70, 1, 1)
+    geoms = [
+        dict(in_h=1, in_w=1, in_c=64, out_c=70),                  # K = 2
+        dict(in_h=3, in_w=3, in_c=32, out_c=65, n=17),            # K = 9
+        dict(in_h=7, in_w=7, in_c=20, out_c=33, n=5),             # K = 49
+        dict(in_h=5, in_w=5, in_c=40, out_c=9, n=33),             # K = 50
+        dict(in_h=3, in_w=3, in_c=96, out_c=40, n=20),            # K = 27
+        dict(in_h=1, in_w=1, in_c=96, out_c=130, n=1),            # K = 3
+        dict(in_h=1, in_w=1, in_c=32, out_c=64, n=16),            # K = 1
+        dict(in_h=2, in_w=3, in_c=7, out_c=200, n=18),            # K = 6, 7 channels
+    ]
+    out = []
+    for gi, g in enumerate(geoms):
+        assert (g["in_h"] * g["in_w"] * ((g["in_c"] + 31) // 32)) % 4 != 0
+        for form in ("xnor", "and"):
+            kw = dict(g, kernel_h=g["in_h"], kernel_w=g["in_w"], type=form, name=f"fc_tail{gi}_{form}")
+            out.append(base.with_(**kw))
+            if gi % 2 == 0:
+                out.append(base.with_(**dict(kw, name=kw["name"] + "_beta", use_beta=True, neuron="relu",
+                                             iscale_dist=("uniform", 0.5, 1.5),
+                                             ibias_dist=("normal", 0.0, 0.2))))
+    return out
+
+
+FC_TAIL = _fc_tail_layers()
+
+
+@pytest.mark.parametrize("layer", FC_TAIL, ids=[l.name for l in FC_TAIL])
+def test_fc_partial_k_step(dev, layer):
+    """The matrix kernel's partial last K step: fp32 output and window sums
+    (matrix route and generic kernel), sign-bit output, and (without beta /
+    affine) packed input; every output compared with the oracle."""
+    assert layer.is_fc
+    inputs = workloads.make_inputs(layer, 9100 + FC_TAIL.index(layer))
+    _log(f"fc tail {layer}")
+    ref = oracle.bconv_layer(layer, inputs)
+    got = parity.run_gpu(layer, inputs, dev)
+    assert got["main_kernel"].startswith("bgemm_kernel"), got["main_kernel"]
+    parity.compare(layer, inputs, got, ref=ref)
+    parity.compare(layer, inputs, parity.run_gpu(layer, inputs, dev, generic=True), ref=ref)
+    words, out, kernel = _run_bits(layer, inputs, dev)
+    assert np.array_equal(parity.unpack_words(words, layer.out_c), (~(out < 0)).astype(np.uint8)), kernel
+    parity.compare_bits(layer, inputs, words, ref=ref)
+    if not layer.use_beta:
+        pw = workloads.make_packed_input(layer, 9200 + FC_TAIL.index(layer))
+        _check_packed(layer, inputs, pw, _packed_run(layer, inputs, pw, dev))
+
+
+@pytest.mark.parametrize("layer", FC_TAIL[:4], ids=[l.name for l in FC_TAIL[:4]])
+def test_fc_partial_k_step_int8(dev, layer):
+    """The same shapes through the int8 matrix-core comparison path."""
+    inputs = workloads.make_inputs(layer, 9100 + FC_TAIL.index(layer))
+    ref = oracle.bconv_layer(layer, inputs)
+    got = parity.run_gpu(layer, inputs, dev, int8_mfma=True)
+    assert got["main_kernel"] == "i8mma_kernel"
+    parity.compare(layer, inputs, got, ref=ref)
