@@ -228,6 +228,23 @@ bconv_status_t bconv_workspace_layout(bconv_t h, int32_t n, bconv_workspace_layo
 bconv_status_t bconv_forward(bconv_t h, void *stream, int32_t n, const float *in, float *out,
                              void *workspace, size_t workspace_bytes);
 
+/* Bytes of the built-in workspace of bconv_forward_noalloc (16 MiB, one copy
+ * per GPU, held until the process ends). */
+#define BCONV_SCRATCH_MAX_BYTES (16u << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): as
+ * bconv_forward, but the workspace is the library's built-in device array of
+ * BCONV_SCRATCH_MAX_BYTES bytes instead of a caller buffer.  Allocates nothing
+ * and calls no allocating routine; the array's address on each GPU is taken
+ * once, when the first handle is created there.  `in` and `out` are the
+ * caller's device buffers as in bconv_forward.  Every call on one GPU shares
+ * that GPU's array, so calls that overlap in time on one GPU (two streams,
+ * two threads) race and give wrong results: serialise them.  Errors: those of
+ * bconv_forward, and WORKSPACE when the batch needs more than
+ * BCONV_SCRATCH_MAX_BYTES of workspace (bconv_workspace_size tells how much). */
+bconv_status_t bconv_forward_noalloc(bconv_t h, void *stream, int32_t n, const float *in, float *out);
+
 /* As bconv_forward, but writes the window sums instead of the epilogue:
  * int32 for XNOR (the +-1 sum over in-image taps) and AND (the 0/1 sum);
  * float for binaryWeights.  Same shape as the output. */

@@ -21,7 +21,7 @@ from ._binding import (  # noqa: F401  (re-exported C ABI names)
     BCONV_NEURON_NONE, BCONV_NEURON_RELU, BCONV_OK, BCONV_XNOR, NEURON_CODES, TYPE_CODES,
     BconvError, BconvLibraryMissing, bconv_calibrate_popcount, bconv_create, bconv_create_fc, bconv_desc_t,
     bconv_destroy,
-    bconv_forward, bconv_forward_accum, bconv_forward_bits, bconv_forward_bits_profiled, bconv_forward_packed,
+    BCONV_SCRATCH_MAX_BYTES, bconv_forward, bconv_forward_accum, bconv_forward_bits, bconv_forward_noalloc, bconv_forward_bits_profiled, bconv_forward_packed,
     bconv_forward_packed_bits, bconv_forward_profiled,
     bconv_get_info, bconv_last_error,
     bconv_main_kernel, bconv_status_string, bconv_validate_desc, bconv_workspace_layout,

@@ -42,6 +42,7 @@ NEURON_NAMES = ("none", "relu", "leaky_relu", "linear", "sigmoid", "hard_sigmoid
 TYPE_CODES = {"binary_weights": BCONV_BINARY_WEIGHTS, "xnor": BCONV_XNOR, "and": BCONV_AND}
 NEURON_CODES = {name: code for code, name in enumerate(NEURON_NAMES)}
 SIZE_MAX = ctypes.c_size_t(-1).value
+BCONV_SCRATCH_MAX_BYTES = 16 << 20
 
 
 class BconvLibraryMissing(RuntimeError):
@@ -97,6 +98,7 @@ def load_library(path: Optional[str] = None):
         "bconv_workspace_size": (st, [vp, i32, ctypes.POINTER(sz)]),
         "bconv_workspace_layout": (st, [vp, i32, ctypes.POINTER(bconv_workspace_layout_t)]),
         "bconv_forward": (st, [vp, vp, i32, vp, vp, vp, sz]),
+        "bconv_forward_noalloc": (st, [vp, vp, i32, vp, vp]),
         "bconv_forward_accum": (st, [vp, vp, i32, vp, vp, vp, sz]),
         "bconv_forward_profiled": (st, [vp, vp, i32, vp, vp, vp, sz, vp, vp]),
         "bconv_forward_bits": (st, [vp, vp, i32, vp, vp, vp, sz]),
@@ -211,6 +213,10 @@ def bconv_workspace_layout(h: int, n: int) -> dict:
 def bconv_forward(h: int, stream, n: int, inp, out, workspace, workspace_bytes: int) -> None:
     _check(load_library().bconv_forward(h, _ptr(stream), n, _ptr(inp), _ptr(out), _ptr(workspace),
                                         workspace_bytes))
+
+
+def bconv_forward_noalloc(h: int, stream, n: int, inp, out) -> None:
+    _check(load_library().bconv_forward_noalloc(h, _ptr(stream), n, _ptr(inp), _ptr(out)))
 
 
 def bconv_forward_accum(h: int, stream, n: int, inp, acc, workspace, workspace_bytes: int) -> None:

@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -327,6 +328,34 @@ bconv_status_t forward_impl(bconv_t h, void *stream, int32_t n, const void *src,
     return BCONV_OK;
 }
 
+// Workspace of bconv_forward_noalloc: a file-scope device array, one copy per
+// GPU, held until the process ends.  Host code never passes `scratch` itself
+// (on the host that name is a stand-in, not a device address): each device's
+// address is taken once with hipGetSymbolAddress, with that device current,
+// and kept in scratch_ptr[].
+__device__ __align__(256) unsigned char scratch[BCONV_SCRATCH_MAX_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void *scratch_ptr[kMaxDevices];
+
+// Address of this device's scratch array; `dev` must be the current device.
+// Resolved on the first call per device (bconv_create calls it at set-up).
+bconv_status_t scratch_for_device(int dev, void **ptr)
+{
+    *ptr = nullptr;
+    if (dev < 0 || dev >= kMaxDevices) return fail(BCONV_ERR_UNSUPPORTED, "device %d beyond the scratch table", dev);
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    if (!scratch_ptr[dev]) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress");
+        scratch_ptr[dev] = p;
+    }
+    *ptr = scratch_ptr[dev];
+    return BCONV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -368,6 +397,14 @@ bconv_status_t bconv_create(const bconv_desc_t *desc, const uint32_t *weight_bit
         return hip_fail(e, "hipGetDevice");
     }
     h->simds = 4 * cus;
+    {
+        // set-up of the scratch-free entry point on this device
+        void *sp = nullptr;
+        if ((st = scratch_for_device(h->device, &sp)) != BCONV_OK) {
+            release(h);
+            return st;
+        }
+    }
 
     const int taps = desc->kernel_h * desc->kernel_w;
     const size_t user_words = (size_t)desc->out_c * taps * h->words;
@@ -490,6 +527,28 @@ bconv_status_t bconv_forward(bconv_t h, void *stream, int32_t n, const float *in
                              void *workspace, size_t workspace_bytes)
 {
     return forward_impl(h, stream, n, in, Source::Values, out, Sink::Output, workspace, workspace_bytes, nullptr,
+                        nullptr);
+}
+
+bconv_status_t bconv_forward_noalloc(bconv_t h, void *stream, int32_t n, const float *in, float *out)
+{
+    if (!h) return fail(BCONV_ERR_INVALID_ARGUMENT, "handle is NULL");
+    if (n < 0) return fail(BCONV_ERR_INVALID_ARGUMENT, "n must be >= 0");
+    const size_t need = layout_for(h, n).total_bytes;
+    if (need > (size_t)BCONV_SCRATCH_MAX_BYTES)
+        return fail(BCONV_ERR_WORKSPACE, "batch %d needs %zu workspace bytes, beyond the %zu of the built-in scratch",
+                    n, need, (size_t)BCONV_SCRATCH_MAX_BYTES);
+    void *ptr = nullptr;
+    {
+        DeviceGuard guard(h->device);
+        if (guard.err != hipSuccess) return hip_fail(guard.err, "hipSetDevice");
+        const bconv_status_t st = scratch_for_device(h->device, &ptr);
+        if (st != BCONV_OK) return st;
+    }
+    // Every byte the kernels read from the workspace is written earlier in
+    // the same call (the pack writes the halo and slack zeros, the convolution
+    // writes beta), so nothing needs clearing between calls.
+    return forward_impl(h, stream, n, in, Source::Values, out, Sink::Output, ptr, BCONV_SCRATCH_MAX_BYTES, nullptr,
                         nullptr);
 }
 
