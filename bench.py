@@ -1,16 +1,22 @@
 #!/usr/bin/env python3
 """Throughput of the binary-convolution forward pass on one MI355X.
 
-One step = one full forward call (pack + A map, beta, convolution with fused
-epilogue) over one batch of the measured layer, inputs already resident in
-HBM.  Prints one JSON line:
+One step = one full forward call (pack + A map, beta, convolution or matrix
+kernel with fused epilogue) over one batch of a measured layer, inputs
+already resident in HBM.  The default run measures all five measured layers
+and prints one JSON line whose headline is the largest of them, the binary
+fully connected layer (256 x 7x7x512 -> 4096, 26.3 G bit-MACs per step):
   value      nominal bit-MACs (N*Ho*Wo*Cout*kh*kw*Cin) per second of whole
              steps, in G bit-MAC/s (= binary GOPS);
-  roofline   the convolution kernel alone, timed by hipEvents that its
+  roofline   the convolution / matrix kernel alone, timed by hipEvents that its
              dispatch records itself (a second pass over the same K steps, so
              the events do not perturb `value`), against whichever peak binds
              it: the VALU popcount peak (XNOR/AND), the bf16 matrix cores at
              three products per fp32 product (binaryWeights), or HBM;
+  pack       the binarise-and-pack kernel (with the A map) of the same steps,
+             timed the same way: algorithmic bytes (fp32 input read once,
+             packed bits and A map written once) per second against HBM;
+  configs    the same figures (and cpu_baseline) for every measured layer;
   comparison    (XNOR / AND) the same layer through the int8 matrix-core
              path (BCONV_FLAG_INT8_MFMA), timed the same way, with its own
              roofline against the dense int8 MFMA peak or HBM; and the layer
@@ -22,13 +28,15 @@ HBM.  Prints one JSON line:
              instructions on registers (the library's calibration kernel, T
              bit-MAC/s; the roofline object adds the kernel's fraction of it
              beside the published peak) and a 1 GiB device copy (GB/s);
-  cpu_baseline  the CPU oracle timed on a bounded sample of the same layer;
+  cpu_baseline  the CPU oracle timed on the layer's whole batch (all host
+             cores), with a one-thread one-image per-core figure;
   cpu_packed_baseline  (XNOR / AND) the packed-bit popcount form on the CPU
              (the oracle package's second reference point), whole batch.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layer I]
-       python bench.py --sweep   (geometry sweep around the bench layer: strides,
-                                  paddings, odd and even kernels; one JSON line)
+       (--layer I: only measured layer I, which is then the headline)
+       python bench.py --sweep   (geometry sweep around the XNOR + beta layer:
+                                  strides, paddings, odd and even kernels; one JSON line)
 """
 
 from __future__ import annotations
@@ -91,14 +99,28 @@ def int8_algorithmic_bytes(layer, n):
     return src + amap + weights + out
 
 
+def pack_algorithmic_bytes(layer, n):
+    """Bytes the binarise-and-pack kernel must move at least: the fp32 input
+    read once, the packed bits (XNOR / AND) and the A map (beta) written once,
+    without the zero halo the library adds around them.  None when the layer
+    has no pack step (binaryWeights without beta)."""
+    pixels = n * layer.in_h * layer.in_w
+    bits = pixels * ((layer.in_c + 31) // 32) * 4 if layer.type != "binary_weights" else 0
+    amap = pixels * 4 if layer.use_beta else 0
+    if not bits and not amap:
+        return None
+    return pixels * layer.in_c * 4 + bits + amap
+
+
 def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--layer", type=int, default=None, help="index into workloads.LAYERS")
-    p.add_argument("--cpu-images", type=int, default=8,
-                   help="images of the layer the oracle runs for cpu_baseline (0: skip)")
+    p.add_argument("--layer", type=int, default=None,
+                   help="measure only this index into workloads.LAYERS (then also the headline)")
+    p.add_argument("--cpu-images", type=int, default=256,
+                   help="at most this many images of each layer for cpu_baseline (0: skip)")
     p.add_argument("--cpu-repeats", type=int, default=3)
     p.add_argument("--no-int8", action="store_true",
                    help="skip the int8 matrix-core comparison (XNOR / AND layers)")
@@ -221,7 +243,7 @@ def run_sweep(args):
             if width and not kernel.endswith(f",{width}>"):
                 conv.close()
                 continue
-            ms, main_ms, out = time_path(pca, torch, np, conv, layer.n, x, stream, args.warmup, args.steps)
+            ms, main_ms, _, out = time_path(pca, torch, np, conv, layer.n, x, stream, args.warmup, args.steps)
             macs = layer.nominal_macs()
             achieved = macs / (main_ms / 1e3) / 1e12
             rows.append({"workload": layer.name, "strip_width": width or "auto", "kernel": kernel,
@@ -236,6 +258,140 @@ def run_sweep(args):
                       "unit": "GOPS (bit-MAC/s)", "peak_unit": "Tbit-MAC/s", "peak": POPCOUNT_PEAK_TBITMAC,
                       "steps": args.steps, "warmup": args.warmup, "n_gpus": 1, "data": "synthetic", "sweep": rows}),
           flush=True)
+
+
+def roofline_of(layer, n, kernel_ms, bits_out=False):
+    """Roofline object of a convolution / matrix kernel that ran `kernel_ms`
+    per launch: whichever of compute and HBM takes longer at peak binds it."""
+    macs = layer.nominal_macs(n)
+    nbytes = algorithmic_bytes(layer, n, bits_out=bits_out)
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+    if layer.type != "binary_weights":
+        t_cmp = macs / (POPCOUNT_PEAK_TBITMAC * 1e12)
+        cmp = ("alu", macs / (kernel_ms / 1e3) / 1e12, POPCOUNT_PEAK_TBITMAC, "Tbit-MAC/s")
+    else:
+        t_cmp = 2 * macs / (BF16X3_PEAK_TFLOPS * 1e12)
+        cmp = ("mfma", 2 * macs / (kernel_ms / 1e3) / 1e12, BF16X3_PEAK_TFLOPS, "TFLOP/s (fp32-exact, bf16x3)")
+    if t_hbm > t_cmp:
+        bound, achieved, peak, unit = "hbm", nbytes / (kernel_ms / 1e3) / 1e9, HBM_PEAK_GBS, "GB/s"
+    else:
+        bound, achieved, peak, unit = cmp
+    return {"bound": bound, "achieved": round(achieved, 3), "peak": round(peak, 3), "unit": unit,
+            "frac": round(achieved / peak, 4), "algorithmic_bytes": nbytes,
+            "avg_kernel_us": round(kernel_ms * 1e3, 3)}
+
+
+def pack_entry(layer, n, pack_ms, kernel):
+    """The pack kernel of the step against HBM: algorithmic bytes per launch
+    over its average dispatch duration."""
+    nb = pack_algorithmic_bytes(layer, n)
+    if nb is None or pack_ms is None:
+        return None
+    achieved = nb / (pack_ms / 1e3) / 1e9
+    return {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "algorithmic_bytes": nb, "avg_kernel_us": round(pack_ms * 1e3, 3),
+            "traffic": recorded_traffic(layer.name + "#pack", kernel)}
+
+
+def measure_layer(pca, torch, np, workloads, index, args, stream):
+    """Every figure of one measured layer: whole steps, its main and pack
+    kernels, the comparisons, and the CPU baselines."""
+    layer = workloads.LAYERS[index]
+    inputs = workloads.make_inputs(layer, workloads.layer_seed(index))
+    dev = torch.device("cuda:0")
+    conv = pca.BinaryConvolution.from_layer(layer, inputs)
+    n = layer.n
+    x = torch.from_numpy(inputs["x"]).to(dev)
+    print(f"# {layer.name}: timing {args.steps} steps", file=sys.stderr, flush=True)
+    ms_per_step, main_ms, pack_ms, out = time_path(pca, torch, np, conv, n, x, stream, args.warmup, args.steps)
+    if args.profile_only:
+        conv.close()
+        return None
+    macs = layer.nominal_macs()
+    binary = layer.type != "binary_weights"
+    kernel = conv.main_kernel(n)
+    unit = "GOPS (bit-MAC/s)" if binary else "GMAC/s (fp32)"
+    entry = {"workload": layer.name, "value": round(macs / (ms_per_step / 1e3) / 1e9, 3), "unit": unit,
+             "ms_per_step": round(ms_per_step, 6), "nominal_macs": macs,
+             "config": {"workload": layer.name, "type": layer.type, "batch": n,
+                        "input_hwc": [layer.in_h, layer.in_w, layer.in_c], "out_c": layer.out_c,
+                        "kernel": [layer.kernel_h, layer.kernel_w],
+                        "stride": [layer.stride_h, layer.stride_w], "pad": [layer.pad_h, layer.pad_w],
+                        "beta": layer.use_beta, "input_affine": layer.iscale_dist is not None,
+                        "neuron": layer.neuron, "parallelism": "none (1 GPU)"},
+             "roofline": dict(kernel=kernel, **roofline_of(layer, n, main_ms),
+                              traffic=recorded_traffic(layer.name, kernel)),
+             "pack": pack_entry(layer, n, pack_ms, pack_kernel_name(layer))}
+    comparison = {}
+    if binary and not args.no_int8:
+        conv8 = pca.BinaryConvolution.from_layer(layer, inputs, int8_mfma=True)
+        ms8, main8, _, out8 = time_path(pca, torch, np, conv8, n, x, stream, args.warmup, args.steps)
+        diff8 = float((out8 - out).abs().max()) if out.numel() else 0.0
+        del out8
+        nb8 = int8_algorithmic_bytes(layer, n)
+        if nb8 / (HBM_PEAK_GBS * 1e9) > macs / (INT8_PEAK_TMAC * 1e12):
+            r8 = ("hbm", nb8 / (main8 / 1e3) / 1e9, HBM_PEAK_GBS, "GB/s")
+        else:
+            r8 = ("mfma", macs / (main8 / 1e3) / 1e12, INT8_PEAK_TMAC, "TMAC/s (int8)")
+        k8 = conv8.main_kernel(n)
+        comparison["int8_mfma"] = {
+            "value": round(macs / (ms8 / 1e3) / 1e9, 3), "unit": unit,
+            "ms_per_step": round(ms8, 6), "kernel": k8, "avg_kernel_us": round(main8 * 1e3, 3),
+            "kernel_speed_vs_popcount": round(main_ms / main8, 4),
+            "max_abs_diff_vs_popcount_output": diff8,
+            "roofline": {"bound": r8[0], "achieved": round(r8[1], 3), "peak": r8[2], "unit": r8[3],
+                         "frac": round(r8[1] / r8[2], 4), "algorithmic_bytes": nb8,
+                         "traffic": recorded_traffic(layer.name + "#int8_mfma", k8)}}
+        conv8.close()
+    if not args.no_bits:
+        msb, mainb, _, outb = time_path(pca, torch, np, conv, n, x, stream, args.warmup, args.steps, bits=True)
+        del outb
+        comparison["packed_bits_output"] = {
+            "value": round(macs / (msb / 1e3) / 1e9, 3), "unit": unit,
+            "ms_per_step": round(msb, 6), "kernel": kernel, "avg_kernel_us": round(mainb * 1e3, 3),
+            "output_bytes": (n * layer.out_h * layer.out_w * ((layer.out_c + 31) // 32) * 4),
+            "roofline": roofline_of(layer, n, mainb, bits_out=True)}
+    if (binary and not layer.use_beta and layer.iscale_dist is None and layer.ibias_dist is None
+            and not args.no_bits):
+        words = torch.from_numpy(workloads.make_packed_input(layer, workloads.layer_seed(index) + 77).view(np.int32))
+        words = words.to(dev)
+        msp = {fmt: time_packed(pca, torch, conv, n, words, stream, args.warmup, args.steps, fmt == "bits")
+               for fmt in ("fp32", "bits")}
+        del words
+        comparison["packed_input"] = {
+            "what": "bconv_forward_packed: input given as packed sign bits (a previous binary layer's output), "
+                    "so the step is repad + convolution, without the fp32 pack",
+            "input_bytes": n * layer.in_h * layer.in_w * layer.words * 4,
+            "fp32_output": {"value": round(macs / (msp["fp32"] / 1e3) / 1e9, 3), "unit": unit,
+                            "ms_per_step": round(msp["fp32"], 6)},
+            "bits_output": {"value": round(macs / (msp["bits"] / 1e3) / 1e9, 3), "unit": unit,
+                            "ms_per_step": round(msp["bits"], 6)}}
+    if comparison:
+        entry["comparison"] = comparison
+    del out
+    conv.close()
+    if args.cpu_images > 0:
+        print(f"# {layer.name}: CPU oracle", file=sys.stderr, flush=True)
+        entry["cpu_baseline"] = cpu_baseline(layer, inputs, min(args.cpu_images, n), args.cpu_repeats)
+        if binary and layer.neuron in ("none", "relu"):
+            entry["cpu_packed_baseline"] = cpu_packed_baseline(layer, inputs, args.cpu_repeats)
+    else:
+        entry["cpu_baseline"] = None
+    return entry
+
+
+def pack_kernel_name(layer):
+    """Name of the binarise-and-pack kernel the library launches for a layer
+    (the fast path takes in_c % 4 == 0 with 16-byte aligned arrays, which torch
+    allocations are)."""
+    if pack_algorithmic_bytes(layer, 1) is None:
+        return None
+    if layer.in_c % 4:
+        return "pack_kernel"
+    seg = 1
+    while seg < (layer.in_c + 3) // 4 and seg < 64:
+        seg <<= 1
+    return f"pack_vec4<{seg},4>"
 
 
 def main():
@@ -257,137 +413,50 @@ def main():
     if args.sweep:
         run_sweep(args)
         return
-    index = workloads.LAYERS.index(workloads.BENCH_LAYER) if args.layer is None else args.layer
-    layer = workloads.LAYERS[index]
-    inputs = workloads.make_inputs(layer, workloads.layer_seed(index))
-    dev = torch.device("cuda:0")
-    conv = pca.BinaryConvolution.from_layer(layer, inputs)
-    n = layer.n
-    x = torch.from_numpy(inputs["x"]).to(dev)
     # a dedicated stream at the default priority
     stream = torch.cuda.Stream()
-    ms_per_step, main_ms, out = time_path(pca, torch, np, conv, n, x, stream, args.warmup, args.steps)
-    conv8 = None
-    if layer.type != "binary_weights" and not args.no_int8:
-        conv8 = pca.BinaryConvolution.from_layer(layer, inputs, int8_mfma=True)
-        ms8, main8, out8 = time_path(pca, torch, np, conv8, n, x, stream, args.warmup, args.steps)
-        diff8 = float((out8 - out).abs().max()) if out.numel() else 0.0
-        del out8
-    if not args.no_bits:
-        msb, mainb, outb = time_path(pca, torch, np, conv, n, x, stream, args.warmup, args.steps, bits=True)
-        del outb
-    packed_ok = (layer.type != "binary_weights" and not layer.use_beta and layer.iscale_dist is None
-                 and layer.ibias_dist is None and not args.profile_only and not args.no_bits)
-    if packed_ok:
-        words = torch.from_numpy(workloads.make_packed_input(layer, workloads.layer_seed(index) + 77).view(np.int32))
-        words = words.to(dev)
-        msp = {fmt: time_packed(pca, torch, conv, n, words, stream, args.warmup, args.steps, fmt == "bits")
-               for fmt in ("fp32", "bits")}
-        del words
+    indices = range(len(workloads.LAYERS)) if args.layer is None else [args.layer]
+    head_index = workloads.LAYERS.index(workloads.HEADLINE_LAYER) if args.layer is None else args.layer
+    entries = {i: measure_layer(pca, torch, np, workloads, i, args, stream) for i in indices}
     if args.copy_mib > 0:
-        src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device=dev)
+        src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
     if args.profile_only:
         return
-    macs = layer.nominal_macs()
-    value = macs / (ms_per_step / 1e3) / 1e9
-    binary = layer.type != "binary_weights"
-    # the roofline is whichever of compute and HBM takes longer at peak
-    nbytes = algorithmic_bytes(layer, n)
-    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
-    if binary:
-        t_cmp = macs / (POPCOUNT_PEAK_TBITMAC * 1e12)
-        cmp = ("alu", macs / (main_ms / 1e3) / 1e12, POPCOUNT_PEAK_TBITMAC, "Tbit-MAC/s")
-    else:
-        t_cmp = 2 * macs / (BF16X3_PEAK_TFLOPS * 1e12)
-        cmp = ("mfma", 2 * macs / (main_ms / 1e3) / 1e12, BF16X3_PEAK_TFLOPS, "TFLOP/s (fp32-exact, bf16x3)")
-    if t_hbm > t_cmp:
-        bound, achieved, peak, runit = "hbm", nbytes / (main_ms / 1e3) / 1e9, HBM_PEAK_GBS, "GB/s"
-    else:
-        bound, achieved, peak, runit = cmp
-    kernel = conv.main_kernel(n)
-    traffic = recorded_traffic(layer.name, kernel)
+    head = entries[head_index]
     line = {
         "metric": "binary conv GOPS (bit-MACs/s) and % of VALU popcount peak, 1 MI355X",
-        "value": round(value, 3),
-        "unit": "GOPS (bit-MAC/s)" if binary else "GMAC/s (fp32)",
+        "value": head["value"],
+        "unit": head["unit"],
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 6),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "u32" if binary else "f32",
+        "dtype": "u32" if workloads.LAYERS[head_index].type != "binary_weights" else "f32",
         "data": "synthetic (seeded; weight bits Bernoulli(0.5))",
-        "config": {"workload": layer.name, "type": layer.type, "batch": n,
-                   "input_hwc": [layer.in_h, layer.in_w, layer.in_c], "out_c": layer.out_c,
-                   "kernel": [layer.kernel_h, layer.kernel_w],
-                   "stride": [layer.stride_h, layer.stride_w], "pad": [layer.pad_h, layer.pad_w],
-                   "beta": layer.use_beta, "input_affine": layer.iscale_dist is not None,
-                   "neuron": layer.neuron, "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": bound, "kernel": kernel, "achieved": round(achieved, 3),
-                     "peak": round(peak, 3), "unit": runit,
-                     "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "algorithmic_bytes": nbytes,
-                     "avg_kernel_us": round(main_ms * 1e3, 3)},
+        "config": head["config"],
+        "roofline": head["roofline"],
+        "pack": head["pack"],
+        "cpu_baseline": head["cpu_baseline"],
     }
-    if conv8 is not None:
-        nb8 = int8_algorithmic_bytes(layer, n)
-        if nb8 / (HBM_PEAK_GBS * 1e9) > macs / (INT8_PEAK_TMAC * 1e12):
-            r8 = ("hbm", nb8 / (main8 / 1e3) / 1e9, HBM_PEAK_GBS, "GB/s")
-        else:
-            r8 = ("mfma", macs / (main8 / 1e3) / 1e12, INT8_PEAK_TMAC, "TMAC/s (int8)")
-        k8 = conv8.main_kernel(n)
-        line["comparison"] = {"int8_mfma": {
-            "value": round(macs / (ms8 / 1e3) / 1e9, 3), "unit": line["unit"],
-            "ms_per_step": round(ms8, 6), "kernel": k8,
-            "avg_kernel_us": round(main8 * 1e3, 3),
-            "kernel_speed_vs_popcount": round(main_ms / main8, 4),
-            "max_abs_diff_vs_popcount_output": diff8,
-            "roofline": {"bound": r8[0], "achieved": round(r8[1], 3), "peak": r8[2], "unit": r8[3],
-                         "frac": round(r8[1] / r8[2], 4), "algorithmic_bytes": nb8,
-                         "traffic": recorded_traffic(layer.name + "#int8_mfma", k8)}}}
-        conv8.close()
-    if not args.no_bits:
-        nbb = algorithmic_bytes(layer, n, bits_out=True)
-        if nbb / (HBM_PEAK_GBS * 1e9) > t_cmp:
-            rb = ("hbm", nbb / (mainb / 1e3) / 1e9, HBM_PEAK_GBS, "GB/s")
-        elif binary:
-            rb = ("alu", macs / (mainb / 1e3) / 1e12, POPCOUNT_PEAK_TBITMAC, "Tbit-MAC/s")
-        else:
-            rb = ("mfma", 2 * macs / (mainb / 1e3) / 1e12, BF16X3_PEAK_TFLOPS, "TFLOP/s (fp32-exact, bf16x3)")
-        line.setdefault("comparison", {})["packed_bits_output"] = {
-            "value": round(macs / (msb / 1e3) / 1e9, 3), "unit": line["unit"],
-            "ms_per_step": round(msb, 6), "kernel": kernel, "avg_kernel_us": round(mainb * 1e3, 3),
-            "output_bytes": (n * layer.out_h * layer.out_w * ((layer.out_c + 31) // 32) * 4),
-            "roofline": {"bound": rb[0], "achieved": round(rb[1], 3), "peak": rb[2], "unit": rb[3],
-                         "frac": round(rb[1] / rb[2], 4), "algorithmic_bytes": nbb}}
-    if packed_ok:
-        line.setdefault("comparison", {})["packed_input"] = {
-            "what": "bconv_forward_packed: input given as packed sign bits (a previous binary layer's output), "
-                    "so the step is repad + convolution, without the fp32 pack",
-            "input_bytes": n * layer.in_h * layer.in_w * layer.words * 4,
-            "fp32_output": {"value": round(macs / (msp["fp32"] / 1e3) / 1e9, 3), "unit": line["unit"],
-                            "ms_per_step": round(msp["fp32"], 6)},
-            "bits_output": {"value": round(macs / (msp["bits"] / 1e3) / 1e9, 3), "unit": line["unit"],
-                            "ms_per_step": round(msp["bits"], 6)}}
+    for key in ("cpu_packed_baseline", "comparison"):
+        if key in head:
+            line[key] = head[key]
     if not args.no_calibration:
         cal = calibrate(pca, torch, stream)
         line["calibration"] = cal
-        if bound == "alu":
-            mp = cal["popcount_peak"]["value"]
-            line["roofline"]["measured_peak"] = mp
-            line["roofline"]["frac_of_measured_peak"] = round(achieved / mp, 4)
-    if args.cpu_images > 0:
-        line["cpu_baseline"] = cpu_baseline(layer, inputs, min(args.cpu_images, n), args.cpu_repeats)
-        if binary and layer.neuron in ("none", "relu"):
-            line["cpu_packed_baseline"] = cpu_packed_baseline(layer, inputs, args.cpu_repeats)
-    else:
-        line["cpu_baseline"] = None
-    conv.close()
+        mp = cal["popcount_peak"]["value"]
+        for e in entries.values():
+            if e["roofline"]["bound"] == "alu":
+                e["roofline"]["measured_peak"] = mp
+                e["roofline"]["frac_of_measured_peak"] = round(e["roofline"]["achieved"] / mp, 4)
+    line["configs"] = [{k: v for k, v in e.items() if k not in ("comparison", "config")}
+                       | {"comparison": e.get("comparison")} for i, e in sorted(entries.items())]
     print(json.dumps(line), flush=True)
 
 
@@ -435,8 +504,9 @@ def calibrate(pca, torch, stream):
 def time_path(pca, torch, np, conv, n, x, stream, warmup, steps, bits=False):
     """Warm up, then (1) time `steps` whole forward calls between two stream
     events, (2) run the same steps again with hipEvents recorded by the main
-    kernel's own dispatch.  Returns (ms per step, mean main-kernel ms, output).
-    With `bits` the output is the packed sign-bit form (bconv_forward_bits)."""
+    kernel's and the input step's own dispatches.  Returns (ms per step, mean
+    main-kernel ms, mean input-step ms or None, output).  With `bits` the
+    output is the packed sign-bit form (bconv_forward_bits)."""
     dev = x.device
     if bits:
         out = torch.empty((n, conv.out_h, conv.out_w, (conv.out_c + 31) // 32), dtype=torch.int32, device=dev)
@@ -461,17 +531,22 @@ def time_path(pca, torch, np, conv, n, x, stream, warmup, steps, bits=False):
     torch.cuda.synchronize()
 
     # timed region 2: the same K steps, each with hipEvents recorded by the
-    # main kernel's dispatch itself (hipExtLaunchKernelGGL) -> its duration
-    begins = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    for e in begins + ends:
-        e.record(stream)  # creates the underlying hipEvent
+    # input step's and the main kernel's dispatches themselves
+    # (hipExtLaunchKernelGGL) -> their durations
+    # binaryWeights without beta launches no input step
+    has_input = conv.type != pca.BCONV_BINARY_WEIGHTS or bool(conv.flags & pca.BCONV_FLAG_USE_BETA_SCALING)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4 if has_input else 2)] for _ in range(steps)]
+    for e in ev:
+        for k in e:
+            k.record(stream)  # creates the underlying hipEvent
     torch.cuda.synchronize()
-    for i in range(steps):
-        fwd_prof(conv.handle, sptr, n, x, out, ws, ws_bytes, begins[i].cuda_event, ends[i].cuda_event)
+    for e in ev:
+        fwd_prof(conv.handle, sptr, n, x, out, ws, ws_bytes, e[0].cuda_event, e[1].cuda_event,
+                 e[2].cuda_event if has_input else None, e[3].cuda_event if has_input else None)
     torch.cuda.synchronize()
-    main_ms = float(np.mean([b.elapsed_time(e) for b, e in zip(begins, ends)]))
-    return t0.elapsed_time(t1) / steps, main_ms, out
+    main_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    pack_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev])) if has_input else None
+    return t0.elapsed_time(t1) / steps, main_ms, pack_ms, out
 
 
 def time_packed(pca, torch, conv, n, words, stream, warmup, steps, bits_out):

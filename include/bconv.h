@@ -251,12 +251,16 @@ bconv_status_t bconv_forward_noalloc(bconv_t h, void *stream, int32_t n, const f
 bconv_status_t bconv_forward_accum(bconv_t h, void *stream, int32_t n, const float *in,
                                    void *acc, void *workspace, size_t workspace_bytes);
 
-/* As bconv_forward, and records the hipEvent_t `main_begin` / `main_end`
- * (either may be NULL) on `stream` immediately before and after the launch of
- * the convolution / matrix kernel, so a caller can time that kernel alone. */
+/* As bconv_forward, and records hipEvent_t's on `stream` (any may be NULL) at
+ * the start and end of two dispatches, so a caller can time each kernel alone:
+ * `main_begin` / `main_end` bracket the convolution / matrix kernel,
+ * `input_begin` / `input_end` the input step before it (the binarise-and-pack
+ * kernel with the A map, or the int8 pack of BCONV_FLAG_INT8_MFMA; binaryWeights
+ * has no input step without beta, and then these two are not recorded). */
 bconv_status_t bconv_forward_profiled(bconv_t h, void *stream, int32_t n, const float *in,
                                       float *out, void *workspace, size_t workspace_bytes,
-                                      void *main_begin, void *main_end);
+                                      void *main_begin, void *main_end, void *input_begin,
+                                      void *input_end);
 
 /* As bconv_forward, but the convolution's epilogue writes packed sign bits of
  * its fp32 output instead of the values, in the input encoding of a next
@@ -276,7 +280,7 @@ bconv_status_t bconv_forward_bits(bconv_t h, void *stream, int32_t n, const floa
 bconv_status_t bconv_forward_bits_profiled(bconv_t h, void *stream, int32_t n, const float *in,
                                            uint32_t *out_bits, void *workspace,
                                            size_t workspace_bytes, void *main_begin,
-                                           void *main_end);
+                                           void *main_end, void *input_begin, void *input_end);
 
 /* Forward pass from input that is already binarised and packed, as a previous
  * layer's bconv_forward_bits writes it (Apple "MPSCNNBinaryConvolution",

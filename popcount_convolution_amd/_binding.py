@@ -100,9 +100,9 @@ def load_library(path: Optional[str] = None):
         "bconv_forward": (st, [vp, vp, i32, vp, vp, vp, sz]),
         "bconv_forward_noalloc": (st, [vp, vp, i32, vp, vp]),
         "bconv_forward_accum": (st, [vp, vp, i32, vp, vp, vp, sz]),
-        "bconv_forward_profiled": (st, [vp, vp, i32, vp, vp, vp, sz, vp, vp]),
+        "bconv_forward_profiled": (st, [vp, vp, i32, vp, vp, vp, sz, vp, vp, vp, vp]),
         "bconv_forward_bits": (st, [vp, vp, i32, vp, vp, vp, sz]),
-        "bconv_forward_bits_profiled": (st, [vp, vp, i32, vp, vp, vp, sz, vp, vp]),
+        "bconv_forward_bits_profiled": (st, [vp, vp, i32, vp, vp, vp, sz, vp, vp, vp, vp]),
         "bconv_main_kernel": (ctypes.c_char_p, [vp, i32]),
         "bconv_forward_packed": (st, [vp, vp, i32, vp, vp, vp, sz]),
         "bconv_forward_packed_bits": (st, [vp, vp, i32, vp, vp, vp, sz]),
@@ -225,10 +225,11 @@ def bconv_forward_accum(h: int, stream, n: int, inp, acc, workspace, workspace_b
 
 
 def bconv_forward_profiled(h: int, stream, n: int, inp, out, workspace, workspace_bytes: int,
-                           main_begin=None, main_end=None) -> None:
+                           main_begin=None, main_end=None, input_begin=None, input_end=None) -> None:
     _check(load_library().bconv_forward_profiled(h, _ptr(stream), n, _ptr(inp), _ptr(out),
                                                  _ptr(workspace), workspace_bytes,
-                                                 _ptr(main_begin), _ptr(main_end)))
+                                                 _ptr(main_begin), _ptr(main_end),
+                                                 _ptr(input_begin), _ptr(input_end)))
 
 
 def bconv_forward_bits(h: int, stream, n: int, inp, out_bits, workspace, workspace_bytes: int) -> None:
@@ -237,10 +238,11 @@ def bconv_forward_bits(h: int, stream, n: int, inp, out_bits, workspace, workspa
 
 
 def bconv_forward_bits_profiled(h: int, stream, n: int, inp, out_bits, workspace, workspace_bytes: int,
-                                main_begin=None, main_end=None) -> None:
+                                main_begin=None, main_end=None, input_begin=None, input_end=None) -> None:
     _check(load_library().bconv_forward_bits_profiled(h, _ptr(stream), n, _ptr(inp), _ptr(out_bits),
                                                       _ptr(workspace), workspace_bytes,
-                                                      _ptr(main_begin), _ptr(main_end)))
+                                                      _ptr(main_begin), _ptr(main_end),
+                                                      _ptr(input_begin), _ptr(input_end)))
 
 
 def bconv_forward_packed(h: int, stream, n: int, in_bits, out, workspace, workspace_bytes: int) -> None:

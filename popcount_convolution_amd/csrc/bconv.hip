@@ -226,7 +226,8 @@ enum class Sink { Output, Accum, Bits };
 enum class Source { Values, Bits };
 
 bconv_status_t forward_impl(bconv_t h, void *stream, int32_t n, const void *src, Source source, void *dst,
-                            Sink sink, void *workspace, size_t workspace_bytes, void *ev_begin, void *ev_end)
+                            Sink sink, void *workspace, size_t workspace_bytes, void *ev_begin, void *ev_end,
+                            void *ev_pack_begin = nullptr, void *ev_pack_end = nullptr)
 {
     if (!h) return fail(BCONV_ERR_INVALID_ARGUMENT, "handle is NULL");
     if (n < 0) return fail(BCONV_ERR_INVALID_ARGUMENT, "n must be >= 0");
@@ -278,15 +279,16 @@ bconv_status_t forward_impl(bconv_t h, void *stream, int32_t n, const void *src,
     float *beta = L.beta_offset == SIZE_MAX ? nullptr : reinterpret_cast<float *>(ws + L.beta_offset);
 
     hipError_t e;
+    const bconv::Launch first{s, static_cast<hipEvent_t>(ev_pack_begin), static_cast<hipEvent_t>(ev_pack_end)};
     if (source == Source::Bits) {
-        e = bconv::launch_repad(g, s, static_cast<const uint32_t *>(src), bits);
+        e = bconv::launch_repad(g, first, static_cast<const uint32_t *>(src), bits);
         if (e != hipSuccess) return hip_fail(e, "repad kernel");
     } else if (h->i8) {
-        e = bconv::launch_pack_i8(g, s, in, h->d_in_scale, h->d_in_bias, h->type == BCONV_AND,
+        e = bconv::launch_pack_i8(g, first, in, h->d_in_scale, h->d_in_bias, h->type == BCONV_AND,
                                   reinterpret_cast<int8_t *>(bits), a_map);
         if (e != hipSuccess) return hip_fail(e, "int8 pack kernel");
     } else if (bits || a_map) {
-        e = bconv::launch_pack(g, s, in, h->d_in_scale, h->d_in_bias, bits, a_map);
+        e = bconv::launch_pack(g, first, in, h->d_in_scale, h->d_in_bias, bits, a_map);
         if (e != hipSuccess) return hip_fail(e, "pack kernel");
     }
     bconv::Epilogue ep{};
@@ -561,10 +563,10 @@ bconv_status_t bconv_forward_accum(bconv_t h, void *stream, int32_t n, const flo
 
 bconv_status_t bconv_forward_profiled(bconv_t h, void *stream, int32_t n, const float *in, float *out,
                                       void *workspace, size_t workspace_bytes, void *main_begin,
-                                      void *main_end)
+                                      void *main_end, void *input_begin, void *input_end)
 {
     return forward_impl(h, stream, n, in, Source::Values, out, Sink::Output, workspace, workspace_bytes, main_begin,
-                        main_end);
+                        main_end, input_begin, input_end);
 }
 
 bconv_status_t bconv_forward_bits(bconv_t h, void *stream, int32_t n, const float *in, uint32_t *out_bits,
@@ -576,10 +578,10 @@ bconv_status_t bconv_forward_bits(bconv_t h, void *stream, int32_t n, const floa
 
 bconv_status_t bconv_forward_bits_profiled(bconv_t h, void *stream, int32_t n, const float *in,
                                            uint32_t *out_bits, void *workspace, size_t workspace_bytes,
-                                           void *main_begin, void *main_end)
+                                           void *main_begin, void *main_end, void *input_begin, void *input_end)
 {
     return forward_impl(h, stream, n, in, Source::Values, out_bits, Sink::Bits, workspace, workspace_bytes, main_begin,
-                        main_end);
+                        main_end, input_begin, input_end);
 }
 
 bconv_status_t bconv_forward_packed(bconv_t h, void *stream, int32_t n, const uint32_t *in_bits, float *out,

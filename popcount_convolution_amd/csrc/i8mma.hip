@@ -355,7 +355,7 @@ hipError_t launch_prepack_i8(const Geom &g, hipStream_t s, const uint32_t *user_
     return hipGetLastError();
 }
 
-hipError_t launch_pack_i8(const Geom &g, hipStream_t s, const float *x, const float *in_scale, const float *in_bias,
+hipError_t launch_pack_i8(const Geom &g, const Launch &L, const float *x, const float *in_scale, const float *in_bias,
                           int and_mode, int8_t *act, float *a_map)
 {
     I8PackArgs a{};
@@ -390,9 +390,8 @@ hipError_t launch_pack_i8(const Geom &g, hipStream_t s, const float *x, const fl
     const long long blocks = (waves + 3) / 4;
     if (blocks == 0) return hipSuccess;
     const bool vec = g.in_c % 4 == 0 && (uintptr_t)x % 16 == 0;
-    if (vec) hipLaunchKernelGGL(pack_i8_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(pack_i8_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, a);
-    return hipGetLastError();
+    if (vec) return launch_kernel(L, pack_i8_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, a);
+    return launch_kernel(L, pack_i8_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, a);
 }
 
 const char *i8mma_kernel_name() { return "i8mma_kernel"; }

@@ -191,11 +191,11 @@ __device__ __forceinline__ int window_valid_taps(int oy, int ox, int sh, int sw,
 }
 
 // Launchers (each returns the hipGetLastError() of its launch).
-hipError_t launch_pack(const Geom &g, hipStream_t s, const float *x, const float *in_scale,
+hipError_t launch_pack(const Geom &g, const Launch &L, const float *x, const float *in_scale,
                        const float *in_bias, uint32_t *bits, float *a_map);
 // Copies caller-packed input bits ([n][in_h][in_w][words]) into the padded bit
 // buffer, zeroing the halo, the slack and the bits past in_c.
-hipError_t launch_repad(const Geom &g, hipStream_t s, const uint32_t *src, uint32_t *bits);
+hipError_t launch_repad(const Geom &g, const Launch &L, const uint32_t *src, uint32_t *bits);
 hipError_t launch_prepack(const Geom &g, hipStream_t s, const uint32_t *user_bits, uint32_t *lane_words,
                           int32_t *lane_popc, float *pm_weights, int pm_cols, int type);
 // Returns true when a specialised convolution kernel exists for this shape.
@@ -231,7 +231,7 @@ int i8_cpad(int in_c);  // channels padded to a multiple of 64
 size_t i8_act_bytes(const Geom &g);
 size_t i8_frag_bytes(const Geom &g);
 hipError_t launch_prepack_i8(const Geom &g, hipStream_t s, const uint32_t *user_bits, void *frag, int and_mode);
-hipError_t launch_pack_i8(const Geom &g, hipStream_t s, const float *x, const float *in_scale, const float *in_bias,
+hipError_t launch_pack_i8(const Geom &g, const Launch &L, const float *x, const float *in_scale, const float *in_bias,
                           int and_mode, int8_t *act, float *a_map);
 const char *i8mma_kernel_name();
 // Calibration kernel: blocks x 256 lanes, each running iters rounds of eight

@@ -286,32 +286,30 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a)
 }
 
 template <int VEC, int SEG>
-hipError_t launch_pack_t(PackArgs a, long long pack_blocks, long long halo_blocks, hipStream_t s)
+hipError_t launch_pack_t(PackArgs a, long long pack_blocks, long long halo_blocks, const Launch &L)
 {
     if (pack_blocks + halo_blocks > 0x7fffffffLL) return hipErrorInvalidValue;
     a.pack_blocks = (int)pack_blocks;
-    hipLaunchKernelGGL((pack_kernel<VEC, SEG>), dim3((unsigned)(pack_blocks + halo_blocks)), dim3(256), 0, s, a);
-    return hipGetLastError();
+    return launch_kernel(L, pack_kernel<VEC, SEG>, dim3((unsigned)(pack_blocks + halo_blocks)), dim3(256), 0, a);
 }
 
 constexpr int kPackPasses = 4;  // wave passes per wave in the vec4 path
 
 template <int SEG>
-hipError_t launch_vec4_t(PackArgs a, long long halo_blocks, hipStream_t s)
+hipError_t launch_vec4_t(PackArgs a, long long halo_blocks, const Launch &L)
 {
     const long long per_wave = (64 / SEG) * kPackPasses;
     const long long waves = (long long)a.n * a.in_h * ((a.in_w + per_wave - 1) / per_wave);
     const long long pack_blocks = (waves + 3) / 4;
     if (pack_blocks + halo_blocks > 0x7fffffffLL) return hipErrorInvalidValue;
     a.pack_blocks = (int)pack_blocks;
-    hipLaunchKernelGGL((pack_vec4<SEG, kPackPasses>), dim3((unsigned)(pack_blocks + halo_blocks)), dim3(256),
-                       0, s, a);
-    return hipGetLastError();
+    return launch_kernel(L, pack_vec4<SEG, kPackPasses>, dim3((unsigned)(pack_blocks + halo_blocks)), dim3(256), 0,
+                         a);
 }
 
 }  // namespace
 
-hipError_t launch_pack(const Geom &g, hipStream_t s, const float *x, const float *in_scale,
+hipError_t launch_pack(const Geom &g, const Launch &s, const float *x, const float *in_scale,
                        const float *in_bias, uint32_t *bits, float *a_map)
 {
     PackArgs a{};
@@ -411,7 +409,7 @@ __global__ __launch_bounds__(256) void repad_kernel(RepadArgs a)
 
 }  // namespace
 
-hipError_t launch_repad(const Geom &g, hipStream_t s, const uint32_t *src, uint32_t *bits)
+hipError_t launch_repad(const Geom &g, const Launch &L, const uint32_t *src, uint32_t *bits)
 {
     const long long image_words = (long long)g.bits_rows * g.bits_cols * g.words;
     const long long total = (long long)g.n * image_words + g.bits_slack_words;
@@ -430,8 +428,7 @@ hipError_t launch_repad(const Geom &g, hipStream_t s, const uint32_t *src, uint3
     a.halo_h = g.bits_halo_h;
     a.halo_w = g.bits_halo_w;
     a.tail_mask = g.in_c % 32 ? (1u << (g.in_c % 32)) - 1u : 0xffffffffu;
-    hipLaunchKernelGGL(repad_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a);
-    return hipGetLastError();
+    return launch_kernel(L, repad_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, a);
 }
 
 }  // namespace bconv

@@ -59,3 +59,22 @@ def test_kernel_source_hash(tmp_path, monkeypatch):
     assert a != bench._kernel_sha("bgemm_kernel<false>")
     assert bench.recorded_traffic("no such workload", "xconv_fast<3,3,4,1,7>") is None
     assert bench.recorded_traffic(workloads.BENCH_LAYER.name, "bgemm_kernel<false>") is None
+
+
+def test_pack_algorithmic_bytes():
+    """fp32 input read once, packed bits and A map written once, without the
+    halo: the per-layer minimum pack bytes, counted by hand."""
+    L = workloads.LAYERS
+    assert bench.pack_algorithmic_bytes(L[0], 1) == 16 * 16 * 64 * 4 + 16 * 16 * 2 * 4 == 67_584
+    assert bench.pack_algorithmic_bytes(L[1], 8) == 8 * 56 * 56 * (128 * 4 + 4 * 4 + 4) == 13_346_816
+    assert bench.pack_algorithmic_bytes(L[2], 32) == 32 * 28 * 28 * (256 * 4 + 8 * 4) == 26_492_928
+    assert bench.pack_algorithmic_bytes(L[3], 16) is None  # binaryWeights without beta: no pack step
+    assert bench.pack_algorithmic_bytes(L[4], 256) == 256 * 49 * (512 * 4 + 16 * 4) == 26_492_928
+    assert bench.pack_kernel_name(L[1]) == "pack_vec4<32,4>"
+    assert bench.pack_kernel_name(L[3]) is None
+
+
+def test_headline_is_the_largest_layer():
+    """The default line quotes the layer with the most bit-MACs per step."""
+    biggest = max(workloads.LAYERS, key=lambda l: l.nominal_macs())
+    assert workloads.HEADLINE_LAYER is biggest and biggest.is_fc
