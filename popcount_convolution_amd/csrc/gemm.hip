@@ -9,15 +9,21 @@
 // (AND); the fused epilogue then applies scale*beta + bias and the neuron.
 //
 // Mapping on gfx950: M = batch rows, N = output channels, K = words.
-//  * A workgroup owns a tile of 64 channels (one per lane) by MR rows; its
-//    four waves each take a quarter of K and the partial sums meet in LDS.
+//  * A workgroup owns a tile of 64 channels (one per lane) by MR = 8 rows; its
+//    four waves each take a quarter of K and the partial sums meet in LDS,
+//    where each wave then finishes two of the rows (sum, epilogue, store).
 //  * A row's activation words are the same for every lane: scalar loads
 //    bring MR rows x 4 words into SGPRs per step and v_xor/v_and take them as
 //    the scalar operand; the lane's 4 weight words come from a K-major table
-//    with one 16-byte load per lane (256 contiguous bytes per wave).
-//  * Workgroups are numbered so that the eight XCDs (workgroups are dealt to
-//    them round-robin) each work on an eighth of the channel tiles, which
-//    keeps each XCD's share of the weight matrix resident in its own L2.
+//    with one 16-byte load per lane (256 contiguous bytes per wave).  Eight
+//    rows keep a wave's registers small enough for eight waves per SIMD
+//    (2048 workgroups for the 256 x 4096 layer), which hides the per-step
+//    memory round trip far better than 16 rows at four waves per SIMD.
+//  * Workgroups are numbered so that each of the eight XCDs (workgroups are
+//    dealt to them round-robin) owns an eighth of the channel tiles, keeping
+//    its share of the weight matrix in its own L2, and so that the workgroups
+//    a compute unit receives together share one row group: their activation
+//    words then hit in the scalar cache.
 #include "internal.h"
 
 namespace bconv {
@@ -25,7 +31,7 @@ namespace {
 
 typedef const uint32_t __attribute__((address_space(4))) *scalar_u32_ptr;
 
-constexpr int kMR = 16;   // batch rows per workgroup
+constexpr int kMR = 8;    // batch rows per workgroup
 constexpr int kWaves = 4; // waves per workgroup (K quarters)
 constexpr int kXcds = 8;  // workgroup dealing period across XCDs
 
@@ -48,18 +54,20 @@ struct GArgs {
 template <bool AND>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void bgemm_kernel(GArgs a)
 {
-    __shared__ int32_t part[kWaves - 1][kMR][64];
+    constexpr int kRowsPerWave = kMR / kWaves;
+    __shared__ int32_t part[kWaves][kMR][64];
     __shared__ float rbeta[kMR];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    // XCD-aware numbering: block b runs on XCD b % 8; give XCD x the channel
-    // tiles x, x+8, x+16, ...
+    // XCD-aware numbering: block b runs on XCD b % 8.  XCD x owns the channel
+    // tiles x, x+8, x+16, ...; consecutive blocks of one XCD (which its
+    // dispatcher spreads over its compute units) walk the row groups of one
+    // tile, so the blocks a compute unit holds at once share their rows.
     const unsigned b = blockIdx.x;
     const unsigned xcd = b % kXcds, local = b / kXcds;
-    const unsigned tiles_per_xcd = ((unsigned)a.tiles + kXcds - 1) / kXcds;
-    const unsigned tile = xcd + kXcds * (local % tiles_per_xcd);
-    const unsigned mg = local / tiles_per_xcd;
-    if (tile >= (unsigned)a.tiles || mg >= (unsigned)a.mgroups) return;  // whole block uniform
+    const unsigned mg = local % (unsigned)a.mgroups;
+    const unsigned tile = xcd + kXcds * (local / (unsigned)a.mgroups);
+    if (tile >= (unsigned)a.tiles) return;  // whole block uniform
     const int m0 = mg * kMR;
 
     // this wave's quarter of the K steps (4 words per step)
@@ -125,23 +133,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void b
         rbeta[lane] = be;
         if (tile == 0 && m0 + lane < a.n) a.beta_out[m0 + lane] = be;
     }
-    if (wave > 0) {
 #pragma unroll
-        for (int r = 0; r < kMR; ++r) part[wave - 1][r][lane] = (int32_t)acc[r];
-    }
+    for (int r = 0; r < kMR; ++r) part[wave][r][lane] = (int32_t)acc[r];
     __syncthreads();
-    if (wave != 0) return;
+    // wave w finishes rows w*kRowsPerWave ... (the sum over the four K quarters
+    // in a fixed order, then the epilogue)
     const int co = tile * kTile + lane;
     const bool co_ok = co < a.out_c;
     if (!co_ok && !a.bits_out) return;  // the sign-bit path needs every lane
     const float sc = a.scale ? (co_ok ? a.scale[co] : 0.0f) : a.scale_value;
     const float bi = a.bias ? (co_ok ? a.bias[co] : 0.0f) : 0.0f;
 #pragma unroll
-    for (int r = 0; r < kMR; ++r) {
+    for (int i = 0; i < kRowsPerWave; ++i) {
+        const int r = wave * kRowsPerWave + i;
         if (m0 + r >= a.n) break;
-        int s = (int)acc[r];
+        int s = 0;
 #pragma unroll
-        for (int w = 0; w < kWaves - 1; ++w) s += part[w][r][lane];
+        for (int w = 0; w < kWaves; ++w) s += part[w][r][lane];
         const int v = AND ? s : a.kbits - 2 * s;
         const long long o = (long long)(m0 + r) * a.out_c + co;
         if (a.acc_out) {
