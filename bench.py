@@ -391,7 +391,8 @@ def pack_kernel_name(layer):
     seg = 1
     while seg < (layer.in_c + 3) // 4 and seg < 64:
         seg <<= 1
-    return f"pack_vec4<{seg},4>"
+    nc = 1 if layer.in_c <= 4 * seg else (2 if layer.in_c <= 8 * seg else 0)
+    return f"pack_vec4<{seg},{2 if nc == 2 else 4},{nc}>"
 
 
 def main():

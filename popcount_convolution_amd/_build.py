@@ -28,6 +28,9 @@ HIPCC_FLAGS = [
     "-fno-gpu-flush-denormals-to-zero",
     # no packed fp32 VALU forms in generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # leading scalar kernel arguments arrive preloaded in SGPRs (kernels whose
+    # first argument is a struct are unaffected)
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wall", "-Wno-unused-function",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]

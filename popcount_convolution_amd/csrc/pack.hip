@@ -137,85 +137,109 @@ __device__ __forceinline__ float group_sum(float v)
 // are spread over SEG lanes, four consecutive channels (one float4) per lane
 // and SEG*4 channels per chunk; a wave pass covers 64/SEG pixels and a wave
 // makes U passes, so it owns a run of G*U consecutive pixels of one image
-// row, located once with scalar arithmetic (no per-lane division).  Loads and
-// stores go through buffer descriptors: a scalar base plus a lane offset.  The
-// input scale and bias of a lane's channels are loaded once per chunk.  A
-// 32-channel word is the OR of 8 lanes' 4-bit groups (DPP), |x'| is summed per
-// lane and then over the pixel's lanes in a fixed order.
-template <int SEG, int U>
-__global__ __launch_bounds__(256) void pack_vec4(PackArgs a)
+// row, located once with scalar arithmetic (no per-lane division).  Without a
+// halo the whole batch is one row (the host passes in_w = all pixels), so runs
+// never stop short at row ends.  NC > 0 fixes the chunk count at compile time:
+// a lane then issues all U*NC of its 16-byte loads before using any.  Loads and
+// stores go through buffer descriptors: a scalar base plus a lane offset.
+// The arguments the first loads need come first, as scalars, so the hardware
+// preloads them into SGPRs before the wave starts (no kernel-argument round
+// trip before the input is requested); the rest are in `a`, fetched while
+// the input loads are in flight.  A 32-channel word is the OR of 8 lanes'
+// 4-bit groups (DPP), |x'| is summed per lane and then over the pixel's
+// lanes in a fixed order.
+template <int SEG, int U, int NC>
+__global__ __launch_bounds__(256) void pack_vec4(const float *x, const float *in_scale, const float *in_bias,
+                                                 int x_bytes, int in_c, int in_w, int row_count, int runs_per_row,
+                                                 int pack_blocks, PackArgs a)
 {
-    if ((int)blockIdx.x >= a.pack_blocks) {
-        clear_halo(a, (long long)(blockIdx.x - a.pack_blocks) * blockDim.x + threadIdx.x);
+    if ((int)blockIdx.x >= pack_blocks) {
+        clear_halo(a, (long long)(blockIdx.x - pack_blocks) * blockDim.x + threadIdx.x);
         return;
     }
     constexpr int G = 64 / SEG;
     constexpr int RUN = G * U;  // pixels per wave
     constexpr int LPW = SEG < 8 ? SEG : 8;
+    constexpr int NCH = NC > 0 ? NC : 1;
     const int lane = threadIdx.x & 63;
     const int slot = lane / SEG;
     const int sl = lane % SEG;
     // wave -> (image row, run of RUN pixels in it); all uniform
     const unsigned wave = blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const unsigned runs_per_row = ((unsigned)a.in_w + RUN - 1) / RUN;
-    const unsigned row_id = wave / runs_per_row;  // img * in_h + y
-    if (row_id >= (unsigned)a.n * (unsigned)a.in_h) return;
-    const int x0 = (int)(wave - row_id * runs_per_row) * RUN;
-    const unsigned img = row_id / (unsigned)a.in_h;
-    const unsigned y = row_id - img * (unsigned)a.in_h;
-    const uint32_t in_base = (row_id * (unsigned)a.in_w + (unsigned)x0) * (unsigned)a.in_c * 4u;
-    const uint32_t pad_base = ((img * (unsigned)a.rows + y + (unsigned)a.halo_h) * (unsigned)a.cols +
-                               (unsigned)(x0 + a.halo_w));  // padded pixel index of x0
-    const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, a.x_bytes);
-    const bool affine = a.in_scale != nullptr || a.in_bias != nullptr;
+    const unsigned row_id = wave / (unsigned)runs_per_row;  // img * in_h + y
+    if (row_id >= (unsigned)row_count) return;
+    const int x0 = (int)(wave - row_id * (unsigned)runs_per_row) * RUN;
+    const uint32_t in_base = (row_id * (unsigned)in_w + (unsigned)x0) * (unsigned)in_c * 4u;
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, x_bytes);
+    const bool affine = in_scale != nullptr || in_bias != nullptr;
     float asum[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) asum[u] = 0.0f;
-    for (int c0 = 0; c0 < a.in_c; c0 += SEG * 4) {
-        const int c = c0 + sl * 4;
-        const bool cact = c < a.in_c;
-        float4 s4 = make_float4(1.f, 1.f, 1.f, 1.f), b4 = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (cact && a.in_scale) s4 = *reinterpret_cast<const float4 *>(a.in_scale + c);
-        if (cact && a.in_bias) b4 = *reinterpret_cast<const float4 *>(a.in_bias + c);
-        float4 v[U];
+    for (int c00 = 0; c00 < in_c; c00 += NCH * SEG * 4) {
+        float4 v[NCH][U], s4[NCH], b4[NCH];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int px = x0 + u * G + slot;
-            v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (cact && px < a.in_w)
-                v[u] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                       xr, (uint32_t)((u * G + slot) * a.in_c + c) * 4u, in_base, 0));
-        }
+        for (int k = 0; k < NCH; ++k) {
+            const int c = c00 + k * SEG * 4 + sl * 4;
+            const bool cact = c < in_c;
+            s4[k] = make_float4(1.f, 1.f, 1.f, 1.f);
+            b4[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (cact && in_scale) s4[k] = *reinterpret_cast<const float4 *>(in_scale + c);
+            if (cact && in_bias) b4[k] = *reinterpret_cast<const float4 *>(in_bias + c);
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int px = x0 + u * G + slot;
-            float t[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-            if (affine) {
-                t[0] = __builtin_fmaf(t[0], s4.x, b4.x);
-                t[1] = __builtin_fmaf(t[1], s4.y, b4.y);
-                t[2] = __builtin_fmaf(t[2], s4.z, b4.z);
-                t[3] = __builtin_fmaf(t[3], s4.w, b4.w);
-            }
-            uint32_t nib = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                nib |= (t[j] < 0.0f ? 0u : 1u) << j;
-                asum[u] += fabsf(t[j]);
-            }
-            if (!cact) nib = 0;  // channels past in_c are zero bits, not signs of 0
-            if (a.bits) {
-                const uint32_t word = group_or<LPW>(nib << ((sl * 4) & 31));
-                if (cact && px < a.in_w && (sl % LPW) == 0)
-                    store_through(&a.bits[((long long)pad_base + u * G + slot) * a.words + c / 32], word);
+            for (int u = 0; u < U; ++u) {
+                const int px = x0 + u * G + slot;
+                v[k][u] = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (cact && px < in_w)
+                    v[k][u] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                             xr, (uint32_t)((u * G + slot) * in_c + c) * 4u, in_base, 0));
             }
         }
+        // the store side's geometry, from the argument struct (its loads
+        // overlap the input loads above)
+        const unsigned img = row_id / (unsigned)a.in_h;
+        const unsigned y = row_id - img * (unsigned)a.in_h;
+        const uint32_t pad_base = ((img * (unsigned)a.rows + y + (unsigned)a.halo_h) * (unsigned)a.cols +
+                                   (unsigned)(x0 + a.halo_w));  // padded pixel index of x0
+#pragma unroll
+        for (int k = 0; k < NCH; ++k) {
+            const int c = c00 + k * SEG * 4 + sl * 4;
+            const bool cact = c < in_c;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int px = x0 + u * G + slot;
+                float t[4] = {v[k][u].x, v[k][u].y, v[k][u].z, v[k][u].w};
+                if (affine) {
+                    t[0] = __builtin_fmaf(t[0], s4[k].x, b4[k].x);
+                    t[1] = __builtin_fmaf(t[1], s4[k].y, b4[k].y);
+                    t[2] = __builtin_fmaf(t[2], s4[k].z, b4[k].z);
+                    t[3] = __builtin_fmaf(t[3], s4[k].w, b4[k].w);
+                }
+                uint32_t nib = 0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    nib |= (t[j] < 0.0f ? 0u : 1u) << j;
+                    asum[u] += fabsf(t[j]);
+                }
+                if (!cact) nib = 0;  // channels past in_c are zero bits, not signs of 0
+                if (a.bits) {
+                    const uint32_t word = group_or<LPW>(nib << ((sl * 4) & 31));
+                    if (cact && px < in_w && (sl % LPW) == 0)
+                        store_through(&a.bits[((long long)pad_base + u * G + slot) * a.words + c / 32], word);
+                }
+            }
+        }
+        if (NC > 0) break;  // all chunks done
     }
     if (a.a_map) {
-        const float inv_c = 1.0f / (float)a.in_c;
+        const unsigned img = row_id / (unsigned)a.in_h;
+        const unsigned y = row_id - img * (unsigned)a.in_h;
+        const uint32_t pad_base = ((img * (unsigned)a.rows + y + (unsigned)a.halo_h) * (unsigned)a.cols +
+                                   (unsigned)(x0 + a.halo_w));
+        const float inv_c = 1.0f / (float)in_c;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const float s = group_sum<SEG>(asum[u]);
-            if (sl == 0 && x0 + u * G + slot < a.in_w) store_through(&a.a_map[(long long)pad_base + u * G + slot], s * inv_c);
+            if (sl == 0 && x0 + u * G + slot < in_w) store_through(&a.a_map[(long long)pad_base + u * G + slot], s * inv_c);
         }
     }
 }
@@ -293,18 +317,25 @@ hipError_t launch_pack_t(PackArgs a, long long pack_blocks, long long halo_block
     return launch_kernel(L, pack_kernel<VEC, SEG>, dim3((unsigned)(pack_blocks + halo_blocks)), dim3(256), 0, a);
 }
 
-constexpr int kPackPasses = 4;  // wave passes per wave in the vec4 path
+// Wave passes per wave in the vec4 path: four, or two when a pixel's channels
+// span two chunks (the lane's loads in flight stay at four either way; the
+// kernel trace of the 512-channel fully connected input favours two passes).
+template <int NC>
+constexpr int pack_passes() { return NC == 2 ? 2 : 4; }
 
-template <int SEG>
+template <int SEG, int NC>
 hipError_t launch_vec4_t(PackArgs a, long long halo_blocks, const Launch &L)
 {
+    constexpr int kPackPasses = pack_passes<NC>();
     const long long per_wave = (64 / SEG) * kPackPasses;
-    const long long waves = (long long)a.n * a.in_h * ((a.in_w + per_wave - 1) / per_wave);
+    const long long runs_per_row = (a.in_w + per_wave - 1) / per_wave;
+    const long long waves = (long long)a.n * a.in_h * runs_per_row;
     const long long pack_blocks = (waves + 3) / 4;
     if (pack_blocks + halo_blocks > 0x7fffffffLL) return hipErrorInvalidValue;
     a.pack_blocks = (int)pack_blocks;
-    return launch_kernel(L, pack_vec4<SEG, kPackPasses>, dim3((unsigned)(pack_blocks + halo_blocks)), dim3(256), 0,
-                         a);
+    return launch_kernel(L, pack_vec4<SEG, kPackPasses, NC>, dim3((unsigned)(pack_blocks + halo_blocks)), dim3(256), 0,
+                         a.x, a.in_scale, a.in_bias, a.x_bytes, a.in_c, a.in_w, a.n * a.in_h, (int)runs_per_row,
+                         a.pack_blocks, a);
 }
 
 }  // namespace
@@ -347,14 +378,27 @@ hipError_t launch_pack(const Geom &g, const Launch &s, const float *x, const flo
     int seg = 1;
     while (seg < need && seg < 64) seg <<= 1;
     if (vec4) {
+        // Without a halo the padded buffer is the input's own pixel order:
+        // pack the batch as one row (runs then never stop at a row end).
+        if (g.bits_rows == g.in_h && g.bits_cols == g.in_w) {
+            a.in_w = (int)a.pixels;  // < 2^29 here (x_bytes < 2^31)
+            a.in_h = 1;
+            a.n = 1;
+            a.rows = 1;
+            a.cols = a.in_w;
+            a.image_words = a.pixels * g.words;  // the slack follows the whole batch
+        }
         switch (seg) {
-        case 1: return launch_vec4_t<1>(a, halo_blocks, s);
-        case 2: return launch_vec4_t<2>(a, halo_blocks, s);
-        case 4: return launch_vec4_t<4>(a, halo_blocks, s);
-        case 8: return launch_vec4_t<8>(a, halo_blocks, s);
-        case 16: return launch_vec4_t<16>(a, halo_blocks, s);
-        case 32: return launch_vec4_t<32>(a, halo_blocks, s);
-        default: return launch_vec4_t<64>(a, halo_blocks, s);
+        case 1: return launch_vec4_t<1, 1>(a, halo_blocks, s);
+        case 2: return launch_vec4_t<2, 1>(a, halo_blocks, s);
+        case 4: return launch_vec4_t<4, 1>(a, halo_blocks, s);
+        case 8: return launch_vec4_t<8, 1>(a, halo_blocks, s);
+        case 16: return launch_vec4_t<16, 1>(a, halo_blocks, s);
+        case 32: return launch_vec4_t<32, 1>(a, halo_blocks, s);
+        default:
+            if (g.in_c <= 256) return launch_vec4_t<64, 1>(a, halo_blocks, s);
+            if (g.in_c <= 512) return launch_vec4_t<64, 2>(a, halo_blocks, s);
+            return launch_vec4_t<64, 0>(a, halo_blocks, s);
         }
     }
     const long long waves = (a.pixels + (64 / seg) - 1) / (64 / seg);

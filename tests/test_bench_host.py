@@ -70,7 +70,8 @@ def test_pack_algorithmic_bytes():
     assert bench.pack_algorithmic_bytes(L[2], 32) == 32 * 28 * 28 * (256 * 4 + 8 * 4) == 26_492_928
     assert bench.pack_algorithmic_bytes(L[3], 16) is None  # binaryWeights without beta: no pack step
     assert bench.pack_algorithmic_bytes(L[4], 256) == 256 * 49 * (512 * 4 + 16 * 4) == 26_492_928
-    assert bench.pack_kernel_name(L[1]) == "pack_vec4<32,4>"
+    assert bench.pack_kernel_name(L[1]) == "pack_vec4<32,4,1>"
+    assert bench.pack_kernel_name(L[4]) == "pack_vec4<64,2,2>"
     assert bench.pack_kernel_name(L[3]) is None
 
 
