@@ -321,8 +321,26 @@ def measure_layer(pca, torch, np, workloads, index, args, stream):
                         "neuron": layer.neuron, "parallelism": "none (1 GPU)"},
              "roofline": dict(kernel=kernel, **roofline_of(layer, n, main_ms),
                               traffic=recorded_traffic(layer.name, kernel)),
-             "pack": pack_entry(layer, n, pack_ms, pack_kernel_name(layer))}
+             "pack": pack_entry(layer, n, pack_ms, pack_kernel_name(layer)) if pack_ms is not None else None}
     comparison = {}
+    if kernel.startswith("xconv_small"):
+        # the same layer on the two-kernel path (pack, then the convolution)
+        os.environ["BCONV_SMALL_FUSED"] = "0"
+        try:
+            conv2 = pca.BinaryConvolution.from_layer(layer, inputs)
+        finally:
+            os.environ.pop("BCONV_SMALL_FUSED", None)
+        ms2, main2, pack2, out2 = time_path(pca, torch, np, conv2, n, x, stream, args.warmup, args.steps)
+        same = bool(torch.equal(out2, out))
+        comparison["two_launch"] = {
+            "what": "the same layer as two kernels (binarise-and-pack, then the convolution), the path the "
+                    "single-launch small-layer kernel replaces",
+            "value": round(macs / (ms2 / 1e3) / 1e9, 3), "unit": unit, "ms_per_step": round(ms2, 6),
+            "kernel": conv2.main_kernel(n), "avg_kernel_us": round(main2 * 1e3, 3),
+            "pack_avg_kernel_us": round(pack2 * 1e3, 3) if pack2 is not None else None,
+            "output_bit_identical": same}
+        del out2
+        conv2.close()
     if binary and not args.no_int8:
         conv8 = pca.BinaryConvolution.from_layer(layer, inputs, int8_mfma=True)
         ms8, main8, _, out8 = time_path(pca, torch, np, conv8, n, x, stream, args.warmup, args.steps)
@@ -383,7 +401,7 @@ def measure_layer(pca, torch, np, workloads, index, args, stream):
 def pack_kernel_name(layer):
     """Name of the binarise-and-pack kernel the library launches for a layer
     (the fast path takes in_c % 4 == 0 with 16-byte aligned arrays, which torch
-    allocations are)."""
+    allocations are), or None when it launches none."""
     if pack_algorithmic_bytes(layer, 1) is None:
         return None
     if layer.in_c % 4:
@@ -534,8 +552,10 @@ def time_path(pca, torch, np, conv, n, x, stream, warmup, steps, bits=False):
     # timed region 2: the same K steps, each with hipEvents recorded by the
     # input step's and the main kernel's dispatches themselves
     # (hipExtLaunchKernelGGL) -> their durations
-    # binaryWeights without beta launches no input step
-    has_input = conv.type != pca.BCONV_BINARY_WEIGHTS or bool(conv.flags & pca.BCONV_FLAG_USE_BETA_SCALING)
+    # binaryWeights without beta launches no input step, nor does the
+    # single-launch small-layer kernel (it binarises its own input)
+    has_input = ((conv.type != pca.BCONV_BINARY_WEIGHTS or bool(conv.flags & pca.BCONV_FLAG_USE_BETA_SCALING))
+                 and not conv.main_kernel(n).startswith("xconv_small"))
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4 if has_input else 2)] for _ in range(steps)]
     for e in ev:
         for k in e:

@@ -180,10 +180,17 @@ bconv_status_t bconv_validate_desc(const bconv_desc_t *desc, int32_t type, uint3
  * weights are rearranged on the device into the layouts the kernels read.
  * Synchronous.  On success *out receives a handle to release with
  * bconv_destroy.
- * Two environment variables, read here, fix the kernel choice of the handle
- * (for tests and tuning; results do not depend on them):
+ * Three environment variables, read here, fix the kernel choice of the
+ * handle (for tests and tuning; results do not depend on them):
  *   BCONV_FORCE_GENERIC=1  the shape-generic kernels instead of the
  *                          specialised and matrix routes;
+ *   BCONV_SMALL_FUSED=0    small XNOR / AND layers without beta (1x1 or 3x3
+ *                          window, in_c <= 128, at most 4096 output pixel x
+ *                          64-channel pairs and 2 MiB of input, not the fully
+ *                          connected shape) keep the two-kernel path (pack,
+ *                          then the convolution) instead of the single kernel
+ *                          that binarises its own input (then the workspace
+ *                          is still required but left untouched);
  *   BCONV_STRIP_WIDTH=P    the specialised XNOR / AND convolution processes P
  *                          output pixels per wave when a kernel for that width
  *                          is compiled for the shape (otherwise the width is

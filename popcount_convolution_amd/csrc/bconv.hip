@@ -23,6 +23,7 @@ struct bconv_handle {
     int out_h, out_w, words, tiles;
     int simds;                // SIMD units of the device
     bool force_generic;
+    bool small_fused;         // small layers take the single-launch kernel (BCONV_SMALL_FUSED)
     int strip_width;          // forced strip width of the specialised convolution (0: by cost)
     bconv::LaneWeights lane;  // XNOR / AND
     uint32_t *d_lane_words;
@@ -217,6 +218,13 @@ bool ranges_overlap(const void *a, size_t an, const void *b, size_t bn)
     return a0 < b0 + bn && b0 < a0 + an;
 }
 
+// Whether a call with fp32 input takes the single-launch small-layer kernel.
+bool takes_small(const bconv_handle *h, const bconv::Geom &g)
+{
+    return h->small_fused && !h->force_generic && !h->i8 && h->type != BCONV_BINARY_WEIGHTS && !uses_beta(h) &&
+           bconv::small_route(g);
+}
+
 // Output forms: fp32 values, raw window sums, or packed sign bits of the
 // fp32 values ([n][out_h][out_w][ceil(out_c/32)] words).
 enum class Sink { Output, Accum, Bits };
@@ -280,7 +288,10 @@ bconv_status_t forward_impl(bconv_t h, void *stream, int32_t n, const void *src,
 
     hipError_t e;
     const bconv::Launch first{s, static_cast<hipEvent_t>(ev_pack_begin), static_cast<hipEvent_t>(ev_pack_end)};
-    if (source == Source::Bits) {
+    const bool small = source == Source::Values && takes_small(h, g);
+    if (small) {
+        // one kernel binarises and convolves; nothing is written to the workspace
+    } else if (source == Source::Bits) {
         e = bconv::launch_repad(g, first, static_cast<const uint32_t *>(src), bits);
         if (e != hipSuccess) return hip_fail(e, "repad kernel");
     } else if (h->i8) {
@@ -304,7 +315,11 @@ bconv_status_t forward_impl(bconv_t h, void *stream, int32_t n, const void *src,
         ep.out_words = out_words;
     }
     const bconv::Launch main{s, static_cast<hipEvent_t>(ev_begin), static_cast<hipEvent_t>(ev_end)};
-    if (h->i8) {
+    if (small) {
+        e = bconv::launch_xconv_small(g, main, h->type == BCONV_AND, in, h->d_in_scale, h->d_in_bias, h->lane, ep,
+                                      sink == Sink::Output ? static_cast<float *>(dst) : nullptr,
+                                      sink == Sink::Accum ? static_cast<int32_t *>(dst) : nullptr);
+    } else if (h->i8) {
         e = bconv::launch_i8mma(g, main, reinterpret_cast<const int8_t *>(bits), h->d_i8frag, ep,
                                 sink == Sink::Output ? static_cast<float *>(dst) : nullptr,
                                 sink == Sink::Accum ? static_cast<int32_t *>(dst) : nullptr);
@@ -391,6 +406,8 @@ bconv_status_t bconv_create(const bconv_desc_t *desc, const uint32_t *weight_bit
     h->force_generic = fg && fg[0] == '1';
     const char *sp = getenv("BCONV_STRIP_WIDTH");
     h->strip_width = sp ? atoi(sp) : 0;
+    const char *sf = getenv("BCONV_SMALL_FUSED");
+    h->small_fused = !(sf && sf[0] == '0');
     hipError_t e = hipGetDevice(&h->device);
     int cus = 0;
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h->device);
@@ -616,6 +633,7 @@ const char *bconv_main_kernel(bconv_t h, int32_t n)
     if (h->type == BCONV_BINARY_WEIGHTS)
         return h->force_generic ? bconv::bwconv_kernel_name(g) : bconv::bwmma_kernel_name(g, h->d_in_scale != nullptr);
     if (h->force_generic) return "xconv_generic";
+    if (takes_small(h, g)) return bconv::small_kernel_name(g, h->type == BCONV_AND);
     if (h->gemm) return bconv::gemm_kernel_name(g, h->type == BCONV_AND);
     return bconv::xconv_kernel_name(g);
 }

@@ -204,6 +204,17 @@ const char *xconv_kernel_name(const Geom &g);
 hipError_t launch_xconv(const Geom &g, const Launch &L, int and_mode, const uint32_t *bits,
                         const LaneWeights &w, const Epilogue &e, float *out, int32_t *acc_out,
                         bool allow_fast);
+// Single-launch XNOR / AND convolution for small layers (binarises its own
+// input; no pack kernel, no bit buffer): 1x1 and 3x3 windows, in_c <= 128,
+// not the fully connected shape, at most kSmallMaxWaves (output pixel,
+// 64-channel tile) pairs and kSmallMaxInputBytes of fp32 input.
+constexpr long long kSmallMaxWaves = 4096;
+constexpr long long kSmallMaxInputBytes = 2ll << 20;
+bool small_route(const Geom &g);
+const char *small_kernel_name(const Geom &g, int and_mode);
+hipError_t launch_xconv_small(const Geom &g, const Launch &L, int and_mode, const float *x, const float *in_scale,
+                              const float *in_bias, const LaneWeights &w, const Epilogue &e, float *out,
+                              int32_t *acc_out);
 // Columns of the +-1.0f binaryWeights table (out_c rounded up to the channel block).
 int bwconv_pm_cols(int out_c);
 const char *bwconv_kernel_name(const Geom &g);

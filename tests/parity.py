@@ -29,10 +29,15 @@ TINY = 1e-30
 
 
 @contextmanager
-def force_generic(on: bool, strip_width: int = 0):
+def force_generic(on: bool, strip_width: int = 0, small_fused=None):
     """Handles created inside use the generic convolution kernel, or the
-    specialised one at the given strip width (0: chosen by cost)."""
-    values = {"BCONV_FORCE_GENERIC": "1" if on else "0", "BCONV_STRIP_WIDTH": str(strip_width)}
+    specialised one at the given strip width (0: chosen by cost).  Small
+    layers take the single-launch kernel by default; a forced kernel or
+    strip width, or small_fused=False, keeps them on the two-kernel path."""
+    if small_fused is None:
+        small_fused = not on and not strip_width
+    values = {"BCONV_FORCE_GENERIC": "1" if on else "0", "BCONV_STRIP_WIDTH": str(strip_width),
+              "BCONV_SMALL_FUSED": "1" if small_fused else "0"}
     old = {k: os.environ.get(k) for k in values}
     os.environ.update(values)
     try:
@@ -52,12 +57,14 @@ def slice_inputs(inputs: dict, images) -> dict:
 
 
 def run_gpu(layer: workloads.Layer, inputs: dict, device, generic: bool = False,
-            int8_mfma: bool = False, strip_width: int = 0) -> dict:
+            int8_mfma: bool = False, strip_width: int = 0, small_fused=None) -> dict:
     """Forward and forward_accum through the C ABI; also returns the
     workspace intermediates (bits or int8 values, A map, beta) of the forward
     call.  ``int8_mfma`` selects the int8 matrix-core comparison path;
-    ``strip_width`` forces the specialised convolution's pixels per wave."""
-    with force_generic(generic, strip_width):
+    ``strip_width`` forces the specialised convolution's pixels per wave;
+    ``small_fused`` (None: the library's default) selects or avoids the
+    single-launch small-layer kernel, which writes no workspace intermediates."""
+    with force_generic(generic, strip_width, small_fused):
         conv = pca.BinaryConvolution.from_layer(layer, inputs, int8_mfma=int8_mfma)
     try:
         n = inputs["x"].shape[0]
@@ -77,6 +84,8 @@ def run_gpu(layer: workloads.Layer, inputs: dict, device, generic: bool = False,
                "main_kernel": conv.main_kernel(n)}
         L = pca.bconv_workspace_layout(conv.handle, n)
         wsh = ws.cpu().numpy()
+        if res["main_kernel"].startswith("xconv_small"):
+            return res  # binarised in registers: no bit buffer, A map or beta
         if L["bits_offset"] is not None:
             cnt = n * L["bits_rows"] * L["bits_cols"] * L["bits_words"]
             raw = wsh[L["bits_offset"]:L["bits_offset"] + 4 * cnt]

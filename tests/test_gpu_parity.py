@@ -232,11 +232,16 @@ def test_special_values(dev):
     inputs["x"] = x
     for form in ("xnor", "and"):
         ly = layer.with_(type=form)
-        got = parity.run_gpu(ly, inputs, dev)
         ref = oracle.bconv_layer(ly, inputs)
+        # the pack kernel's bits (two-kernel path) ...
+        got = parity.run_gpu(ly, inputs, dev, small_fused=False)
         assert np.array_equal(got["acc"], ref["acc"])
         ph, pw = got["bits_pad"]
         assert np.array_equal(got["bits"][:, ph:ph + 4, pw:pw + 4], parity.expected_words(ref["signs"], form))
+        # ... and the single-launch kernel's own binarisation
+        got = parity.run_gpu(ly, inputs, dev, small_fused=True)
+        assert got["main_kernel"].startswith("xconv_small")
+        assert np.array_equal(got["acc"], ref["acc"])
 
 
 def test_binary_weights_special_values(dev):
@@ -1017,3 +1022,85 @@ def test_fc_partial_k_step_int8(dev, layer):
     got = parity.run_gpu(layer, inputs, dev, int8_mfma=True)
     assert got["main_kernel"] == "i8mma_kernel"
     parity.compare(layer, inputs, got, ref=ref)
+
+
+# --------------------------------------- single-launch small-layer kernel
+
+def _small_layers():
+    """Small conv layers (1x1 and 3x3 windows, 1 to 4 words per pixel) that
+    the library runs with its single-launch kernel: ragged word and channel
+    tiles, strides, no / centred / one-sided padding, a window with every tap
+    but one in the padding, Cin = 1; XNOR and AND, plain and with the input
+    affine and an activation, and with the scalar output scale."""
+    base = workloads.Layer("small", "xnor", 2, 9, 11, 64, 70, 3, 3, 1, 1, 1, 1)
+    geoms = [
+        dict(in_c=64, out_c=70),
+        dict(n=3, in_c=27, out_c=40),
+        dict(in_c=100, out_c=64, stride_h=2, stride_w=2),
+        dict(in_c=70, out_c=130, pad_h=0, pad_w=0),
+        dict(in_c=96, out_c=33, pad_h=1, pad_w=1, pad_bottom=0, pad_right=0),
+        dict(in_c=33, out_c=9, kernel_h=1, kernel_w=1, pad_h=0, pad_w=0),
+        dict(in_c=128, out_c=64, kernel_h=1, kernel_w=1, pad_h=0, pad_w=0, stride_h=2, stride_w=3),
+        dict(n=1, in_h=1, in_w=1, in_c=64, out_c=8),
+        dict(in_c=1, out_c=3),
+    ]
+    out = []
+    for gi, g in enumerate(geoms):
+        for form in ("xnor", "and"):
+            for variant in range(3):
+                kw = dict(g, type=form, name=f"small{gi}_{form}_v{variant}")
+                if variant == 1:
+                    kw.update(neuron="relu", iscale_dist=("uniform", 0.5, 1.5), ibias_dist=("normal", 0.0, 0.2))
+                elif variant == 2:
+                    kw.update(oscale_dist=None, obias_dist=None, scale_value=0.75, neuron="sigmoid")
+                out.append(base.with_(**kw))
+    return out
+
+
+SMALL_LAYERS = _small_layers()
+
+
+@pytest.mark.parametrize("layer", SMALL_LAYERS, ids=[l.name for l in SMALL_LAYERS])
+def test_small_layer_single_launch(dev, layer):
+    """The single-launch kernel: window sums bit-exact and outputs within the
+    parity bounds of the oracle, bit-identical to the two-kernel path (pack,
+    then the convolution) on the same handle inputs, and sign-bit output."""
+    inputs = workloads.make_inputs(layer, 9400 + SMALL_LAYERS.index(layer))
+    _log(f"small {layer}")
+    ref = oracle.bconv_layer(layer, inputs)
+    got = parity.run_gpu(layer, inputs, dev, small_fused=True)
+    assert got["main_kernel"].startswith("xconv_small"), got["main_kernel"]
+    parity.compare(layer, inputs, got, ref=ref)
+    two = parity.run_gpu(layer, inputs, dev, small_fused=False)
+    assert not two["main_kernel"].startswith("xconv_small")
+    assert np.array_equal(got["acc"], two["acc"])
+    assert np.array_equal(got["out"].view(np.uint32), two["out"].view(np.uint32))
+    with parity.force_generic(False, small_fused=True):
+        words, out, kernel = _run_bits(layer, inputs, dev)
+    assert kernel.startswith("xconv_small")
+    assert np.array_equal(parity.unpack_words(words, layer.out_c), (~(out < 0)).astype(np.uint8))
+    parity.compare_bits(layer, inputs, words, ref=ref)
+
+
+def test_small_route_limits(dev):
+    """Beta layers, the fully connected shape, 5x5 windows, more than 128
+    input channels and large layers keep the two-kernel path."""
+    base = workloads.LAYERS[0]
+    assert base.name.startswith("xnor_conv_b1_16x16")
+    cases = {
+        "default": (base, True),
+        "beta": (base.with_(use_beta=True), False),
+        "fc": (base.with_(kernel_h=16, kernel_w=16, pad_h=0, pad_w=0), False),
+        "k5": (base.with_(kernel_h=5, kernel_w=5, pad_h=2, pad_w=2), False),
+        "c160": (base.with_(in_c=160), False),
+        "large": (workloads.LAYERS[2], False),
+    }
+    for name, (layer, small) in cases.items():
+        inputs = workloads.make_inputs(layer, 31, n=1)
+        with parity.force_generic(False, small_fused=True):
+            conv = pca.BinaryConvolution.from_layer(layer, inputs)
+        try:
+            kernel = conv.main_kernel(layer.n)
+            assert kernel.startswith("xconv_small") == small, (name, kernel)
+        finally:
+            conv.close()
