@@ -10,8 +10,8 @@
 //
 // Mapping on gfx950: M = batch rows, N = output channels, K = words.
 //  * A workgroup owns a tile of 64 channels (one per lane) by MR = 8 rows; its
-//    four waves each take a quarter of K and the partial sums meet in LDS,
-//    where each wave then finishes two of the rows (sum, epilogue, store).
+//    eight waves each take an eighth of K and the partial sums meet in LDS,
+//    where each wave then finishes one of the rows (sum, epilogue, store).
 //  * A row's activation words are the same for every lane: scalar loads
 //    bring MR rows x 4 words into SGPRs per step and v_xor/v_and take them as
 //    the scalar operand; the lane's 4 weight words come from a K-major table
@@ -32,7 +32,7 @@ namespace {
 typedef const uint32_t __attribute__((address_space(4))) *scalar_u32_ptr;
 
 constexpr int kMR = 8;    // batch rows per workgroup
-constexpr int kWaves = 4; // waves per workgroup (K quarters)
+constexpr int kWaves = 8; // waves per workgroup (K eighths)
 constexpr int kXcds = 8;  // workgroup dealing period across XCDs
 
 struct GArgs {
@@ -52,7 +52,7 @@ struct GArgs {
 };
 
 template <bool AND>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void bgemm_kernel(GArgs a)
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4))) void bgemm_kernel(GArgs a)
 {
     constexpr int kRowsPerWave = kMR / kWaves;
     __shared__ int32_t part[kWaves][kMR][64];
@@ -70,7 +70,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void b
     if (tile >= (unsigned)a.tiles) return;  // whole block uniform
     const int m0 = mg * kMR;
 
-    // this wave's quarter of the K steps (4 words per step)
+    // this wave's share of the K steps (4 words per step)
     const int steps = a.k4;
     const int q0 = (steps * wave) / kWaves, q1 = (steps * (wave + 1)) / kWaves;
 
@@ -136,8 +136,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void b
 #pragma unroll
     for (int r = 0; r < kMR; ++r) part[wave][r][lane] = (int32_t)acc[r];
     __syncthreads();
-    // wave w finishes rows w*kRowsPerWave ... (the sum over the four K quarters
-    // in a fixed order, then the epilogue)
+    // wave w finishes rows w*kRowsPerWave ... (the sum over the K shares in a
+    // fixed order, then the epilogue)
     const int co = tile * kTile + lane;
     const bool co_ok = co < a.out_c;
     if (!co_ok && !a.bits_out) return;  // the sign-bit path needs every lane
