@@ -63,17 +63,18 @@ INT8_PEAK_TMAC = 2500.0
 HBM_PEAK_GBS = 8000.0
 
 
-def algorithmic_bytes(layer, n, bits_out=False):
+def algorithmic_bytes(layer, n, bits_out=False, fp32_input=False):
     """Bytes the convolution / matrix kernel must move at least: its input
-    operand once (packed bits for XNOR/AND, fp32 for binaryWeights), the A
-    map when beta is on, the weight bits and the output (fp32, or packed sign
-    bits with `bits_out`)."""
+    operand once (packed bits for XNOR/AND, fp32 for binaryWeights and for
+    the single-launch small-layer kernel, `fp32_input`, which binarises its
+    own input), the A map when beta is on, the weight bits and the output
+    (fp32, or packed sign bits with `bits_out`)."""
     words = (layer.in_c + 31) // 32
     if layer.is_fc:
         rows, cols = layer.in_h, layer.in_w
     else:
         rows, cols = layer.in_h + layer.pad_h + layer.pad_h_end, layer.in_w + layer.pad_w + layer.pad_w_end
-    if layer.type == "binary_weights":
+    if layer.type == "binary_weights" or fp32_input:
         src = n * layer.in_h * layer.in_w * layer.in_c * 4
     else:
         src = n * rows * cols * words * 4
@@ -260,11 +261,11 @@ def run_sweep(args):
           flush=True)
 
 
-def roofline_of(layer, n, kernel_ms, bits_out=False):
+def roofline_of(layer, n, kernel_ms, bits_out=False, kernel=""):
     """Roofline object of a convolution / matrix kernel that ran `kernel_ms`
     per launch: whichever of compute and HBM takes longer at peak binds it."""
     macs = layer.nominal_macs(n)
-    nbytes = algorithmic_bytes(layer, n, bits_out=bits_out)
+    nbytes = algorithmic_bytes(layer, n, bits_out=bits_out, fp32_input=kernel.startswith("xconv_small"))
     t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
     if layer.type != "binary_weights":
         t_cmp = macs / (POPCOUNT_PEAK_TBITMAC * 1e12)
@@ -319,7 +320,7 @@ def measure_layer(pca, torch, np, workloads, index, args, stream):
                         "stride": [layer.stride_h, layer.stride_w], "pad": [layer.pad_h, layer.pad_w],
                         "beta": layer.use_beta, "input_affine": layer.iscale_dist is not None,
                         "neuron": layer.neuron, "parallelism": "none (1 GPU)"},
-             "roofline": dict(kernel=kernel, **roofline_of(layer, n, main_ms),
+             "roofline": dict(kernel=kernel, **roofline_of(layer, n, main_ms, kernel=kernel),
                               traffic=recorded_traffic(layer.name, kernel)),
              "pack": pack_entry(layer, n, pack_ms, pack_kernel_name(layer)) if pack_ms is not None else None}
     comparison = {}
@@ -368,7 +369,7 @@ def measure_layer(pca, torch, np, workloads, index, args, stream):
             "value": round(macs / (msb / 1e3) / 1e9, 3), "unit": unit,
             "ms_per_step": round(msb, 6), "kernel": kernel, "avg_kernel_us": round(mainb * 1e3, 3),
             "output_bytes": (n * layer.out_h * layer.out_w * ((layer.out_c + 31) // 32) * 4),
-            "roofline": roofline_of(layer, n, mainb, bits_out=True)}
+            "roofline": roofline_of(layer, n, mainb, bits_out=True, kernel=kernel)}
     if (binary and not layer.use_beta and layer.iscale_dist is None and layer.ibias_dist is None
             and not args.no_bits):
         words = torch.from_numpy(workloads.make_packed_input(layer, workloads.layer_seed(index) + 77).view(np.int32))
@@ -597,8 +598,9 @@ def time_packed(pca, torch, conv, n, words, stream, warmup, steps, bits_out):
 
 
 # the source file that defines (and launches) each main kernel, by name prefix
-KERNEL_FILES = {"xconv_fast": "xconv_fast.h", "xconv_generic": "xconv.hip", "bgemm": "gemm.hip",
-                "bwmma": "bwmma.hip", "bwconv": "bwconv.hip", "i8mma": "i8mma.hip"}
+KERNEL_FILES = {"xconv_fast": "xconv_fast.h", "xconv_generic": "xconv.hip", "xconv_small": "xconv_small.hip",
+                "bgemm": "gemm.hip", "bwmma": "bwmma.hip", "bwconv": "bwconv.hip", "i8mma": "i8mma.hip",
+                "pack_vec4": "pack.hip", "pack_kernel": "pack.hip"}
 
 
 def _kernel_sha(kernel: str) -> str:
