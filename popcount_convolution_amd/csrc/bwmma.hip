@@ -50,8 +50,10 @@
 //    input buffers keep the loads of the next steps in flight;
 //  * the bf16 weight fragments of the workgroup's channels are staged in
 //    LDS (up to 18 K steps = NB*18 KiB per stage, the first stage requested
-//    at the top of the kernel so it overlaps the prologue), read with one
-//    ds_read_b128 per channel block;
+//    at the top of the kernel so it overlaps the prologue), copied from the
+//    prepacked table straight into LDS (global_load_lds: no register round
+//    trip, no LDS write instructions), read with one ds_read_b128 per
+//    channel block;
 //  * workgroups are dealt to the eight XCDs so that each XCD works on a
 //    contiguous range of output pixels (its L2 then holds the input rows its
 //    windows share).
@@ -341,19 +343,20 @@ __global__ __launch_bounds__(256 * KSPLIT) void bwmma_kernel(MmaArgs a)
     const int mtile = idx / a.ntiles, ntile = idx - (idx / a.ntiles) * a.ntiles;
 
     // The first LDS stage of weight fragments depends only on the channel
-    // tile: request it now, so its latency overlaps the prologue.  Each
-    // thread holds up to kPer fragments until they are written to LDS.
+    // tile: request it now, straight into LDS (each wave's 64 lanes fill 64
+    // consecutive 16-byte entries), so its latency overlaps the prologue.
     constexpr int kPer = (kStage * kStepU4 + kThreads - 1) / kThreads;
     const u32x4 *gfrag = a.frag + (long long)ntile * a.ksteps * kStepU4;
-    u32x4 pre[kPer];
-    {
-        const int total = (a.ksteps < kStage ? a.ksteps : kStage) * kStepU4;
+    auto stage_dma = [&](int s0, int total) {
 #pragma unroll
         for (int b = 0; b < kPer; ++b) {
-            const int i = (int)threadIdx.x + b * kThreads;
-            if (i < total) pre[b] = gfrag[i];
+            const int i0 = wave * 64 + b * kThreads;  // wave-uniform
+            if (i0 < total && i0 + lane < total)
+                __builtin_amdgcn_global_load_lds((const void *)(gfrag + (long long)s0 * kStepU4 + i0 + lane),
+                                                 (__attribute__((address_space(3))) void *)(stage + i0), 16, 0, 0);
         }
-    }
+    };
+    stage_dma(0, (a.ksteps < kStage ? a.ksteps : kStage) * kStepU4);
 
     // this lane's output pixel (pixels past the batch reuse the last one and
     // are not stored)
@@ -398,20 +401,12 @@ __global__ __launch_bounds__(256 * KSPLIT) void bwmma_kernel(MmaArgs a)
             load_step<VEC8, AFFINE>(a, xr, lpos, lane_base, iy0, ix0, cg, live, xbuf[i]);
             advance(a, lpos);
         }
-        const int total = cnt * kStepU4;
-        if (s0 > 0) {  // later stages: all of a thread's fragments requested before any is written
-#pragma unroll
-            for (int b = 0; b < kPer; ++b) {
-                const int i = (int)threadIdx.x + b * kThreads;
-                if (i < total) pre[b] = gfrag[(long long)s0 * kStepU4 + i];
-            }
+        if (s0 > 0) {  // later stages: once the previous one is fully read
+            lds_barrier();
+            stage_dma(s0, cnt * kStepU4);
         }
-        lds_barrier();  // previous stage fully read
-#pragma unroll
-        for (int b = 0; b < kPer; ++b) {
-            const int i = (int)threadIdx.x + b * kThreads;
-            if (i < total) stage[i] = pre[b];
-        }
+        // the stage's copies (and the input loads above) have landed, in every wave
+        __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xf << 8));  // vmcnt(0)
         lds_barrier();
         // Software pipeline over the steps: xbuf[0] and xbuf[1] hold the
         // inputs of the next two unsplit steps; the split of step s+1 runs
