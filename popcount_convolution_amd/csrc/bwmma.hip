@@ -100,6 +100,7 @@ struct MmaArgs {
     int x_bytes, out_bytes;
     int vec_out;  // out_c % 4 == 0 and a 16-byte aligned destination: 16-byte stores
     int vec_params;  // 16-byte aligned scale and bias arrays (or absent): 16-byte loads
+    FastDiv div_hw, div_ow, div_chunks, div_kw;  // by out_h*out_w, out_w, chunks, kw
 };
 
 // Exact three-way bf16 split of 8 floats (see the file comment); element j
@@ -194,8 +195,9 @@ struct StepPos {
 
 __device__ __forceinline__ StepPos step_pos(const MmaArgs &a, int s)
 {
-    const int tap = s / a.chunks;
-    return StepPos{tap / a.kw, tap % a.kw, s % a.chunks};
+    const int tap = (int)fastdiv((uint32_t)s, a.div_chunks);
+    const int ky = (int)fastdiv((uint32_t)tap, a.div_kw);
+    return StepPos{ky, tap - ky * a.kw, s - tap * a.chunks};
 }
 
 __device__ __forceinline__ void advance(const MmaArgs &a, StepPos &p)
@@ -323,8 +325,14 @@ __device__ __forceinline__ void mma_step_split(f32x4 acc[NB], const Pieces &cur,
     for (int j = 0; j < 8; ++j) asm volatile("" ::"v"(nxt.r2[j]));
 }
 
+// The leading scalar arguments (what the weight-stage copies need) arrive
+// preloaded in SGPRs, so the stage is requested before the argument struct
+// is fetched: frag = a.frag, ksteps = a.ksteps, blocks = mtiles*ntiles, per =
+// blocks per XCD, (ntiles, dnt_m, dnt_s, dnt_id) = a.ntiles and its divisor.
 template <bool VEC8, bool AFFINE, int NB, int KSPLIT>
-__global__ __launch_bounds__(256 * KSPLIT) void bwmma_kernel(MmaArgs a)
+__global__ __launch_bounds__(256 * KSPLIT) void bwmma_kernel(const u32x4 *frag, int ksteps, int blocks, int per,
+                                                             int ntiles, uint32_t dnt_m, int dnt_s, uint32_t dnt_id,
+                                                             MmaArgs a)
 {
     constexpr int kThreads = 256 * KSPLIT;
     constexpr int kChanTile = NB * 16;  // output channels per workgroup
@@ -336,17 +344,16 @@ __global__ __launch_bounds__(256 * KSPLIT) void bwmma_kernel(MmaArgs a)
     const int group = wave & 3, kq = wave >> 2;
     // XCD-aware numbering: block b runs on XCD b % 8; XCD x takes the
     // contiguous tile range [x*per, (x+1)*per).
-    const int blocks = a.mtiles * a.ntiles;
-    const int per = (blocks + kXcds - 1) / kXcds;
     const int idx = (int)(blockIdx.x % kXcds) * per + (int)(blockIdx.x / kXcds);
     if (idx >= blocks) return;  // uniform over the workgroup
-    const int mtile = idx / a.ntiles, ntile = idx - (idx / a.ntiles) * a.ntiles;
+    const int mtile = (int)fastdiv((uint32_t)idx, FastDiv{dnt_m, dnt_s, dnt_id});
+    const int ntile = idx - mtile * ntiles;
 
     // The first LDS stage of weight fragments depends only on the channel
     // tile: request it now, straight into LDS (each wave's 64 lanes fill 64
     // consecutive 16-byte entries), so its latency overlaps the prologue.
     constexpr int kPer = (kStage * kStepU4 + kThreads - 1) / kThreads;
-    const u32x4 *gfrag = a.frag + (long long)ntile * a.ksteps * kStepU4;
+    const u32x4 *gfrag = frag + (long long)ntile * ksteps * kStepU4;
     auto stage_dma = [&](int s0, int total) {
 #pragma unroll
         for (int b = 0; b < kPer; ++b) {
@@ -356,7 +363,7 @@ __global__ __launch_bounds__(256 * KSPLIT) void bwmma_kernel(MmaArgs a)
                                                  (__attribute__((address_space(3))) void *)(stage + i0), 16, 0, 0);
         }
     };
-    stage_dma(0, (a.ksteps < kStage ? a.ksteps : kStage) * kStepU4);
+    stage_dma(0, (ksteps < kStage ? ksteps : kStage) * kStepU4);
 
     // this lane's output pixel (pixels past the batch reuse the last one and
     // are not stored)
@@ -364,8 +371,8 @@ __global__ __launch_bounds__(256 * KSPLIT) void bwmma_kernel(MmaArgs a)
     const bool live = p_raw < a.m_total;
     const int pix = live ? p_raw : a.m_total - 1;
     const int hw = a.out_h * a.out_w;
-    const int img = pix / hw, rem = pix - (pix / hw) * hw;
-    const int oy = rem / a.out_w, ox = rem - (rem / a.out_w) * a.out_w;
+    const int img = (int)fastdiv((uint32_t)pix, a.div_hw), rem = pix - img * hw;
+    const int oy = (int)fastdiv((uint32_t)rem, a.div_ow), ox = rem - oy * a.out_w;
     const int iy0 = oy * a.sh - a.ph, ix0 = ox * a.sw - a.pw;
     const int cg = (lane >> 4) * 8;
     const int lane_base = ((img * a.in_h + iy0) * a.in_w + ix0) * a.in_c + cg;
@@ -607,11 +614,15 @@ hipError_t launch_bwmma_t(const Launch &L, const MmaArgs &a, bool vec, bool affi
     const uint32_t stage_bytes = (uint32_t)(a.ksteps < kStage ? a.ksteps : kStage) * kStepBytes;
     const uint32_t lds = stage_bytes > kRed ? stage_bytes : kRed;
     const dim3 gr(grid), bl(256 * KSPLIT);
+    const int blocks = a.mtiles * a.ntiles;
+    const int per = (blocks + kXcds - 1) / kXcds;
+    const FastDiv dn = make_fastdiv((uint32_t)a.ntiles);
+    auto go = [&](auto kernel) {
+        return launch_kernel(L, kernel, gr, bl, lds, a.frag, a.ksteps, blocks, per, a.ntiles, dn.m, dn.s, dn.id, a);
+    };
     if (vec)
-        return affine ? launch_kernel(L, bwmma_kernel<true, true, NB, KSPLIT>, gr, bl, lds, a)
-                      : launch_kernel(L, bwmma_kernel<true, false, NB, KSPLIT>, gr, bl, lds, a);
-    return affine ? launch_kernel(L, bwmma_kernel<false, true, NB, KSPLIT>, gr, bl, lds, a)
-                  : launch_kernel(L, bwmma_kernel<false, false, NB, KSPLIT>, gr, bl, lds, a);
+        return affine ? go(bwmma_kernel<true, true, NB, KSPLIT>) : go(bwmma_kernel<true, false, NB, KSPLIT>);
+    return affine ? go(bwmma_kernel<false, true, NB, KSPLIT>) : go(bwmma_kernel<false, false, NB, KSPLIT>);
 }
 
 hipError_t launch_bwmma(const Geom &g, const Launch &L, const float *x, const float *in_scale, const float *in_bias,
@@ -669,6 +680,10 @@ hipError_t launch_bwmma(const Geom &g, const Launch &L, const float *x, const fl
     const void *dst = acc_out ? (const void *)acc_out : (const void *)out;
     a.vec_out = g.out_c % 4 == 0 && (uintptr_t)dst % 16 == 0;
     a.vec_params = (uintptr_t)e.scale % 16 == 0 && (uintptr_t)e.bias % 16 == 0;
+    a.div_hw = make_fastdiv((uint32_t)(g.out_h * g.out_w));
+    a.div_ow = make_fastdiv((uint32_t)g.out_w);
+    a.div_chunks = make_fastdiv((uint32_t)a.chunks);
+    a.div_kw = make_fastdiv((uint32_t)g.kw);
     const int blocks = a.mtiles * a.ntiles;
     const int grid = (blocks + kXcds - 1) / kXcds * kXcds;
     // input affine: both arrays or neither (the handle fills in a missing one)
