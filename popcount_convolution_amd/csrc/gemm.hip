@@ -51,8 +51,14 @@ struct GArgs {
     int kbits;              // valid bits per row (H*W*Cin)
 };
 
+// The leading scalar arguments (a.bits, a.wflat, the divisor by a.mgroups,
+// a.mgroups, a.tiles, a.k4, a.n, a.K) are what the main loop needs; they
+// arrive preloaded in SGPRs, so the first loads go out before the argument
+// struct (needed only by the epilogue) is fetched.
 template <bool AND>
-__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4))) void bgemm_kernel(GArgs a)
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4))) void bgemm_kernel(
+    const uint32_t *bits, const uint32_t *wflat, uint32_t mg_m, int mg_s, uint32_t mg_id, int mgroups, int tiles,
+    int k4, int n, int K, GArgs a)
 {
     constexpr int kRowsPerWave = kMR / kWaves;
     __shared__ int32_t part[kWaves][kMR][64];
@@ -65,23 +71,23 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4))
     // tile, so the blocks a compute unit holds at once share their rows.
     const unsigned b = blockIdx.x;
     const unsigned xcd = b % kXcds, local = b / kXcds;
-    const unsigned mg = local % (unsigned)a.mgroups;
-    const unsigned tile = xcd + kXcds * (local / (unsigned)a.mgroups);
-    if (tile >= (unsigned)a.tiles) return;  // whole block uniform
+    const unsigned lq = fastdiv(local, FastDiv{mg_m, mg_s, mg_id});
+    const unsigned mg = local - lq * (unsigned)mgroups;
+    const unsigned tile = xcd + kXcds * lq;
+    if (tile >= (unsigned)tiles) return;  // whole block uniform
     const int m0 = mg * kMR;
 
     // this wave's share of the K steps (4 words per step)
-    const int steps = a.k4;
+    const int steps = k4;
     const int q0 = (steps * wave) / kWaves, q1 = (steps * (wave + 1)) / kWaves;
 
     uint32_t acc[kMR];
 #pragma unroll
     for (int r = 0; r < kMR; ++r) acc[r] = 0;
-    const uint4 *wl = reinterpret_cast<const uint4 *>(a.wflat) + (long long)tile * steps * 64 + lane;
+    const uint4 *wl = reinterpret_cast<const uint4 *>(wflat) + (long long)tile * steps * 64 + lane;
     // rows past the batch read the last row (their results are not stored)
-    const int rows_valid = a.n - m0 < kMR ? a.n - m0 : kMR;
-    const scalar_u32_ptr blk = (scalar_u32_ptr)a.bits + (long long)m0 * a.K;
-    const int K = a.K;
+    const int rows_valid = n - m0 < kMR ? n - m0 : kMR;
+    const scalar_u32_ptr blk = (scalar_u32_ptr)bits + (long long)m0 * K;
     const int qfull = K / 4 < q1 ? K / 4 : q1;  // steps with 4 words inside K
 
     if (rows_valid == kMR) {
@@ -248,8 +254,12 @@ hipError_t launch_gemm(const Geom &g, const Launch &L, int and_mode, const uint3
     const long long blocks = (long long)kXcds * tiles_per_xcd * a.mgroups;
     if (blocks == 0) return hipSuccess;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-    if (and_mode) return launch_kernel(L, bgemm_kernel<true>, dim3((unsigned)blocks), dim3(64 * kWaves), 0, a);
-    return launch_kernel(L, bgemm_kernel<false>, dim3((unsigned)blocks), dim3(64 * kWaves), 0, a);
+    const FastDiv dm = make_fastdiv((uint32_t)a.mgroups);
+    auto go = [&](auto kernel) {
+        return launch_kernel(L, kernel, dim3((unsigned)blocks), dim3(64 * kWaves), 0, a.bits, a.wflat, dm.m, dm.s,
+                             dm.id, a.mgroups, a.tiles, a.k4, a.n, a.K, a);
+    };
+    return and_mode ? go(bgemm_kernel<true>) : go(bgemm_kernel<false>);
 }
 
 }  // namespace bconv
