@@ -29,6 +29,7 @@ struct PackArgs {
     long long image_words;  // rows*cols*words
     long long halo_a;       // n*halo_pixels_per_image (A map halo entries)
     int n;
+    FastDiv div_in_h;       // by in_h (image and row of a packed row index)
 };
 
 __device__ __forceinline__ void halo_pixel(const PackArgs &a, unsigned i, int &row, int &col)
@@ -149,8 +150,8 @@ __device__ __forceinline__ float group_sum(float v)
 // 4-bit groups (DPP), |x'| is summed per lane and then over the pixel's
 // lanes in a fixed order.
 template <int SEG, int U, int NC>
-__global__ __launch_bounds__(256) void pack_vec4(const float *x, const float *in_scale, const float *in_bias,
-                                                 int x_bytes, int in_c, int in_w, int row_count, int runs_per_row,
+__global__ __launch_bounds__(256) void pack_vec4(const float *x, int x_bytes, int in_c, int in_w, int row_count,
+                                                 int runs_per_row, uint32_t rpr_m, int rpr_s, uint32_t rpr_id,
                                                  int pack_blocks, PackArgs a)
 {
     if ((int)blockIdx.x >= pack_blocks) {
@@ -166,11 +167,14 @@ __global__ __launch_bounds__(256) void pack_vec4(const float *x, const float *in
     const int sl = lane % SEG;
     // wave -> (image row, run of RUN pixels in it); all uniform
     const unsigned wave = blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const unsigned row_id = wave / (unsigned)runs_per_row;  // img * in_h + y
+    const unsigned row_id = fastdiv(wave, FastDiv{rpr_m, rpr_s, rpr_id});  // img * in_h + y
     if (row_id >= (unsigned)row_count) return;
     const int x0 = (int)(wave - row_id * (unsigned)runs_per_row) * RUN;
     const uint32_t in_base = (row_id * (unsigned)in_w + (unsigned)x0) * (unsigned)in_c * 4u;
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, x_bytes);
+    // the input affine's arrays come with the argument struct; their loads
+    // are only needed once the input has arrived
+    const float *in_scale = a.in_scale, *in_bias = a.in_bias;
     const bool affine = in_scale != nullptr || in_bias != nullptr;
     float asum[U];
 #pragma unroll
@@ -196,7 +200,7 @@ __global__ __launch_bounds__(256) void pack_vec4(const float *x, const float *in
         }
         // the store side's geometry, from the argument struct (its loads
         // overlap the input loads above)
-        const unsigned img = row_id / (unsigned)a.in_h;
+        const unsigned img = fastdiv(row_id, a.div_in_h);
         const unsigned y = row_id - img * (unsigned)a.in_h;
         const uint32_t pad_base = ((img * (unsigned)a.rows + y + (unsigned)a.halo_h) * (unsigned)a.cols +
                                    (unsigned)(x0 + a.halo_w));  // padded pixel index of x0
@@ -231,7 +235,7 @@ __global__ __launch_bounds__(256) void pack_vec4(const float *x, const float *in
         if (NC > 0) break;  // all chunks done
     }
     if (a.a_map) {
-        const unsigned img = row_id / (unsigned)a.in_h;
+        const unsigned img = fastdiv(row_id, a.div_in_h);
         const unsigned y = row_id - img * (unsigned)a.in_h;
         const uint32_t pad_base = ((img * (unsigned)a.rows + y + (unsigned)a.halo_h) * (unsigned)a.cols +
                                    (unsigned)(x0 + a.halo_w));
@@ -333,8 +337,10 @@ hipError_t launch_vec4_t(PackArgs a, long long halo_blocks, const Launch &L)
     const long long pack_blocks = (waves + 3) / 4;
     if (pack_blocks + halo_blocks > 0x7fffffffLL) return hipErrorInvalidValue;
     a.pack_blocks = (int)pack_blocks;
+    const FastDiv rd = make_fastdiv((uint32_t)runs_per_row);
+    a.div_in_h = make_fastdiv((uint32_t)a.in_h);
     return launch_kernel(L, pack_vec4<SEG, kPackPasses, NC>, dim3((unsigned)(pack_blocks + halo_blocks)), dim3(256), 0,
-                         a.x, a.in_scale, a.in_bias, a.x_bytes, a.in_c, a.in_w, a.n * a.in_h, (int)runs_per_row,
+                         a.x, a.x_bytes, a.in_c, a.in_w, a.n * a.in_h, (int)runs_per_row, rd.m, rd.s, rd.id,
                          a.pack_blocks, a);
 }
 
