@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbconv.so")
 # longest compiles first, so they start before the pool fills
-SOURCES = ("xconv_k3.hip", "xconv_k24.hip", "xconv_k5.hip", "xconv_k1.hip", "bwmma.hip", "i8mma.hip", "gemm.hip",
+SOURCES = ("xconv_k3.hip", "xconv_k24.hip", "xconv_k5.hip", "xconv_k1.hip", "bwmma.hip", "i8mma.hip", "gemm.hip", "gemm_f4.hip",
            "xconv.hip", "xconv_small.hip", "bwconv.hip", "bconv.hip", "pack.hip", "prepack.hip", "calib.hip")
 ARCH = "gfx950"
 

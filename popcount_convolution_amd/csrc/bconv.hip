@@ -30,6 +30,8 @@ struct bconv_handle {
     int32_t *d_lane_popc;
     uint32_t *d_flat;         // K-major weights of the fully connected route
     bool gemm;
+    void *d_f4;               // fully connected route on the fp4 matrix cores: weight table and counts
+    bool gemm_popcount;       // keep the fully connected route on the VALU popcount kernel (BCONV_GEMM_POPCOUNT)
     bool i8;                  // int8 matrix-core comparison path (XNOR / AND)
     void *d_i8frag;           // its int8 weight fragments
     float *d_pm;              // binaryWeights, VALU kernel (+-1.0f table)
@@ -205,7 +207,7 @@ bconv_status_t upload(const T *host, size_t count, T **dev)
 void release(bconv_handle *h)
 {
     if (!h) return;
-    void *ptrs[] = {h->d_lane_words, h->d_lane_popc, h->d_flat, h->d_pm, h->d_mma, h->d_i8frag, h->d_out_scale,
+    void *ptrs[] = {h->d_lane_words, h->d_lane_popc, h->d_flat, h->d_f4, h->d_pm, h->d_mma, h->d_i8frag, h->d_out_scale,
                     h->d_out_bias, h->d_in_scale, h->d_in_bias};
     for (void *p : ptrs)
         if (p) (void)hipFree(p);
@@ -331,6 +333,10 @@ bconv_status_t forward_impl(bconv_t h, void *stream, int32_t n, const void *src,
         e = bconv::launch_bwconv(g, main, in, h->d_in_scale, h->d_in_bias, h->d_pm, h->pm_cols, ep,
                                  sink == Sink::Output ? static_cast<float *>(dst) : nullptr,
                                  sink == Sink::Accum ? static_cast<float *>(dst) : nullptr);
+    } else if (h->gemm && !h->force_generic && h->d_f4) {
+        e = bconv::launch_gemm_f4(g, main, h->type == BCONV_AND, bits, h->d_f4, ep,
+                                  sink == Sink::Output ? static_cast<float *>(dst) : nullptr,
+                                  sink == Sink::Accum ? static_cast<int32_t *>(dst) : nullptr);
     } else if (h->gemm && !h->force_generic) {
         e = bconv::launch_gemm(g, main, h->type == BCONV_AND, bits, h->d_flat, ep,
                                sink == Sink::Output ? static_cast<float *>(dst) : nullptr,
@@ -408,6 +414,8 @@ bconv_status_t bconv_create(const bconv_desc_t *desc, const uint32_t *weight_bit
     h->strip_width = sp ? atoi(sp) : 0;
     const char *sf = getenv("BCONV_SMALL_FUSED");
     h->small_fused = !(sf && sf[0] == '0');
+    const char *gp = getenv("BCONV_GEMM_POPCOUNT");
+    h->gemm_popcount = gp && gp[0] == '1';
     hipError_t e = hipGetDevice(&h->device);
     int cus = 0;
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h->device);
@@ -483,6 +491,10 @@ bconv_status_t bconv_create(const bconv_desc_t *desc, const uint32_t *weight_bit
     if (e == hipSuccess && h->gemm) {
         e = hipMalloc(reinterpret_cast<void **>(&h->d_flat), bconv::gemm_weight_words(g) * 4);
         if (e == hipSuccess) e = bconv::launch_prepack_flat(g, nullptr, d_user, h->d_flat);
+    }
+    if (e == hipSuccess && h->gemm && !h->i8 && !h->gemm_popcount && bconv::gemm_f4_route(g)) {
+        e = hipMalloc(&h->d_f4, bconv::gemm_f4_bytes(g));
+        if (e == hipSuccess) e = bconv::launch_prepack_f4(g, nullptr, d_user, h->d_f4);
     }
     if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
     (void)hipFree(d_user);
@@ -634,6 +646,7 @@ const char *bconv_main_kernel(bconv_t h, int32_t n)
         return h->force_generic ? bconv::bwconv_kernel_name(g) : bconv::bwmma_kernel_name(g, h->d_in_scale != nullptr);
     if (h->force_generic) return "xconv_generic";
     if (takes_small(h, g)) return bconv::small_kernel_name(g, h->type == BCONV_AND);
+    if (h->gemm && h->d_f4) return bconv::gemm_f4_kernel_name(h->type == BCONV_AND);
     if (h->gemm) return bconv::gemm_kernel_name(g, h->type == BCONV_AND);
     return bconv::xconv_kernel_name(g);
 }

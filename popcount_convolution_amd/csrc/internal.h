@@ -225,6 +225,14 @@ hipError_t launch_prepack_flat(const Geom &g, hipStream_t s, const uint32_t *use
 const char *gemm_kernel_name(const Geom &g, int and_mode);
 hipError_t launch_gemm(const Geom &g, const Launch &L, int and_mode, const uint32_t *bits, const uint32_t *wflat,
                        const Epilogue &e, float *out, int32_t *acc_out);
+// The same product on the fp4 matrix cores (0/1 bit counts, exact in fp32):
+// taken when the row length in words is a multiple of 4.
+bool gemm_f4_route(const Geom &g);
+size_t gemm_f4_bytes(const Geom &g);
+hipError_t launch_prepack_f4(const Geom &g, hipStream_t s, const uint32_t *user_bits, void *tab);
+const char *gemm_f4_kernel_name(int and_mode);
+hipError_t launch_gemm_f4(const Geom &g, const Launch &L, int and_mode, const uint32_t *bits, const void *tab,
+                          const Epilogue &e, float *out, int32_t *acc_out);
 hipError_t launch_bwconv(const Geom &g, const Launch &L, const float *x, const float *in_scale,
                          const float *in_bias, const float *pm_weights, int pm_cols,
                          const Epilogue &e, float *out, float *acc_out);

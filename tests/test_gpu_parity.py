@@ -1014,6 +1014,69 @@ def test_fc_partial_k_step(dev, layer):
         _check_packed(layer, inputs, pw, _packed_run(layer, inputs, pw, dev))
 
 
+# ------------------------------------- FC product on the fp4 matrix cores
+
+def _fc_f4_layers():
+    """Fully connected shapes whose K = kh*kw*ceil(in_c/32) words is a multiple
+    of 4 (the fp4 matrix-core route): a lone partial 16-word step, full steps
+    only, full steps plus a partial one, batches that leave a ragged 64-row
+    block or a single row, channel counts that leave ragged 16- and 64-channel
+    tiles, and zero bits past Cin inside a pixel's last word; XNOR and AND,
+    plain and with beta + input affine + ReLU."""
+    base = workloads.Layer("fc_f4", "xnor", 17, 1, 1, 128, 70, 1, 1)
+    geoms = [
+        dict(in_h=1, in_w=1, in_c=128, out_c=70, n=17),    # K = 4: one partial step
+        dict(in_h=3, in_w=3, in_c=128, out_c=65, n=65),    # K = 36: 2 steps + 1 word group
+        dict(in_h=2, in_w=2, in_c=256, out_c=130, n=64),   # K = 32: full steps only
+        dict(in_h=7, in_w=7, in_c=512, out_c=100, n=130),  # K = 784: 49 steps, 3 row blocks
+        dict(in_h=4, in_w=4, in_c=100, out_c=1, n=3),      # 4 bits of the last word valid
+        dict(in_h=1, in_w=2, in_c=255, out_c=64, n=1),     # one row
+        dict(in_h=5, in_w=5, in_c=128, out_c=200, n=40),   # K = 100: 6 steps + 1 word group
+    ]
+    out = []
+    for gi, g in enumerate(geoms):
+        assert (g["in_h"] * g["in_w"] * ((g["in_c"] + 31) // 32)) % 4 == 0
+        for form in ("xnor", "and"):
+            kw = dict(g, kernel_h=g["in_h"], kernel_w=g["in_w"], type=form, name=f"fc_f4_{gi}_{form}")
+            out.append(base.with_(**kw))
+            if gi % 2 == 1:
+                out.append(base.with_(**dict(kw, name=kw["name"] + "_beta", use_beta=True, neuron="relu",
+                                             iscale_dist=("uniform", 0.5, 1.5),
+                                             ibias_dist=("normal", 0.0, 0.2))))
+    return out
+
+
+FC_F4 = _fc_f4_layers()
+
+
+@pytest.mark.parametrize("layer", FC_F4, ids=[l.name for l in FC_F4])
+def test_fc_fp4_route(dev, layer):
+    """The fully connected product on the fp4 matrix cores: fp32 output and
+    window sums compared with the oracle on every output; window sums and fp32
+    outputs identical to the VALU popcount GEMM's; sign-bit output; and
+    (without beta / affine) packed input."""
+    assert layer.is_fc
+    seed = 9400 + FC_F4.index(layer)
+    inputs = workloads.make_inputs(layer, seed)
+    _log(f"fc fp4 {layer} seed {seed}")
+    ref = oracle.bconv_layer(layer, inputs)
+    got = parity.run_gpu(layer, inputs, dev)
+    assert got["main_kernel"].startswith("bgemm_f4_kernel"), got["main_kernel"]
+    parity.compare(layer, inputs, got, ref=ref)
+    pop = parity.run_gpu(layer, inputs, dev, gemm_popcount=True)
+    assert pop["main_kernel"].startswith("bgemm_kernel"), pop["main_kernel"]
+    assert np.array_equal(got["acc"], pop["acc"])
+    assert np.array_equal(got["out"].view(np.uint32), pop["out"].view(np.uint32))
+    words, out, kernel = _run_bits(layer, inputs, dev)
+    assert kernel.startswith("bgemm_f4_kernel"), kernel
+    assert np.array_equal(parity.unpack_words(words, layer.out_c), (~(out < 0)).astype(np.uint8)), kernel
+    assert not parity.unpack_words(words, None)[..., layer.out_c:].any(), "output bits past out_c are set"
+    parity.compare_bits(layer, inputs, words, ref=ref)
+    if not layer.use_beta:
+        pw = workloads.make_packed_input(layer, 9500 + FC_F4.index(layer))
+        _check_packed(layer, inputs, pw, _packed_run(layer, inputs, pw, dev))
+
+
 @pytest.mark.parametrize("layer", FC_TAIL[:4], ids=[l.name for l in FC_TAIL[:4]])
 def test_fc_partial_k_step_int8(dev, layer):
     """The same shapes through the int8 matrix-core comparison path."""
