@@ -19,7 +19,9 @@ fully connected layer (256 x 7x7x512 -> 4096, 26.3 G bit-MACs per step):
   configs    the same figures (and cpu_baseline) for every measured layer;
   comparison    (XNOR / AND) the same layer through the int8 matrix-core
              path (BCONV_FLAG_INT8_MFMA), timed the same way, with its own
-             roofline against the dense int8 MFMA peak or HBM; and the layer
+             roofline against the dense int8 MFMA peak or HBM; for the fully
+             connected layer also through the fp4 matrix-core path
+             (BCONV_FLAG_FP4_MFMA), against the dense fp4 peak; and the layer
              with its output written as packed sign bits for a next binary
              layer (bconv_forward_bits), timed the same way; and (XNOR / AND
              without beta or input affine) the layer fed packed sign bits
@@ -60,6 +62,8 @@ POPCOUNT_PEAK_TBITMAC = VALU_LANE_OPS * 16 / 1e12          # 629.1
 BF16X3_PEAK_TFLOPS = 2500.0 / 3
 # dense int8 MFMA: 5.0 POP/s = 2.5e15 multiply-accumulates per second
 INT8_PEAK_TMAC = 2500.0
+# dense fp4 (e2m1) MFMA: 10.1 PFLOP/s
+FP4_PEAK_TFLOPS = 10100.0
 HBM_PEAK_GBS = 8000.0
 
 
@@ -124,7 +128,7 @@ def parse():
                    help="at most this many images of each layer for cpu_baseline (0: skip)")
     p.add_argument("--cpu-repeats", type=int, default=3)
     p.add_argument("--no-int8", action="store_true",
-                   help="skip the int8 matrix-core comparison (XNOR / AND layers)")
+                   help="skip the matrix-core comparisons (int8 for XNOR / AND layers, fp4 for fully connected ones)")
     p.add_argument("--sweep", action="store_true",
                    help="time the convolution over a sweep of strides, paddings and kernel sizes")
     p.add_argument("--sweep-widths", action="store_true",
@@ -282,6 +286,29 @@ def roofline_of(layer, n, kernel_ms, bits_out=False, kernel=""):
             "avg_kernel_us": round(kernel_ms * 1e3, 3)}
 
 
+def fp4_route(layer):
+    """Whether the fp4 matrix-core comparison path takes the layer: XNOR / AND
+    of the fully connected shape with a window of a multiple of 4 words."""
+    return (layer.type != "binary_weights" and layer.is_fc
+            and (layer.kernel_h * layer.kernel_w * ((layer.in_c + 31) // 32)) % 4 == 0)
+
+
+def fp4_roofline(layer, n, kernel_ms):
+    """Roofline of the fp4 matrix-core product: two fp4 operations per
+    bit-MAC against the dense fp4 peak, or HBM, whichever binds at peak; with
+    its rate as a fraction of the VALU popcount peak beside it."""
+    macs = layer.nominal_macs(n)
+    nbytes = algorithmic_bytes(layer, n)
+    if nbytes / (HBM_PEAK_GBS * 1e9) > 2 * macs / (FP4_PEAK_TFLOPS * 1e12):
+        bound, achieved, peak, unit = "hbm", nbytes / (kernel_ms / 1e3) / 1e9, HBM_PEAK_GBS, "GB/s"
+    else:
+        bound, achieved, peak, unit = "mfma", 2 * macs / (kernel_ms / 1e3) / 1e12, FP4_PEAK_TFLOPS, "TFLOP/s (fp4)"
+    bitmacs = macs / (kernel_ms / 1e3) / 1e12
+    return {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "algorithmic_bytes": nbytes, "avg_kernel_us": round(kernel_ms * 1e3, 3),
+            "tbitmac_per_s": round(bitmacs, 3), "of_popcount_peak": round(bitmacs / POPCOUNT_PEAK_TBITMAC, 4)}
+
+
 def pack_entry(layer, n, pack_ms, kernel):
     """The pack kernel of the step against HBM: algorithmic bytes per launch
     over its average dispatch duration."""
@@ -362,6 +389,21 @@ def measure_layer(pca, torch, np, workloads, index, args, stream):
                          "frac": round(r8[1] / r8[2], 4), "algorithmic_bytes": nb8,
                          "traffic": recorded_traffic(layer.name + "#int8_mfma", k8)}}
         conv8.close()
+    if binary and not args.no_int8 and fp4_route(layer):
+        conv4 = pca.BinaryConvolution.from_layer(layer, inputs, fp4_mfma=True)
+        ms4, main4, _, out4 = time_path(pca, torch, np, conv4, n, x, stream, args.warmup, args.steps)
+        same4 = bool(torch.equal(out4, out))
+        del out4
+        k4 = conv4.main_kernel(n)
+        comparison["fp4_mfma"] = {
+            "what": "the fully connected product on the fp4 matrix cores (BCONV_FLAG_FP4_MFMA): the 0/1 bit "
+                    "product count as exact e2m1 products, XNOR from it and the input and weight bit counts",
+            "value": round(macs / (ms4 / 1e3) / 1e9, 3), "unit": unit,
+            "ms_per_step": round(ms4, 6), "kernel": k4, "avg_kernel_us": round(main4 * 1e3, 3),
+            "kernel_speed_vs_popcount": round(main_ms / main4, 4),
+            "output_bit_identical_to_popcount": same4,
+            "roofline": dict(fp4_roofline(layer, n, main4), traffic=recorded_traffic(layer.name + "#fp4_mfma", k4))}
+        conv4.close()
     if not args.no_bits:
         msb, mainb, _, outb = time_path(pca, torch, np, conv, n, x, stream, args.warmup, args.steps, bits=True)
         del outb

@@ -96,12 +96,24 @@ typedef enum {
  * BCONV_FLAG_BETA_VALID_TAPS divides beta's window sum by the count of
  * in-image taps instead of kernel_h * kernel_w (the other reading of the
  * divisor of the page's first beta equation where the window leaves the
- * image; identical inside the image).  Requires BCONV_FLAG_USE_BETA_SCALING. */
+ * image; identical inside the image).  Requires BCONV_FLAG_USE_BETA_SCALING.
+ * BCONV_FLAG_FP4_MFMA selects a second comparison path, on the fp4 matrix
+ * cores, for XNOR and AND layers of the fully connected shape
+ * (MPSCNNFullyConnected, Overview, conditions) whose window holds a multiple
+ * of 4 words (kernel_h * kernel_w * ceil(in_c / 32) % 4 == 0): the product
+ * count of the 0/1 bits, sum_k x_k * w_k, runs as exact e2m1 products with
+ * fp32 accumulation; AND is that count and XNOR follows from it and the
+ * counts of set input and weight bits (popcount(x ^ w) = S_x + S_w - 2 S_xw).
+ * Results are identical (exact integers, the same fp32 epilogue); the
+ * workspace is that of the popcount path.  bconv_create returns
+ * BCONV_ERR_UNSUPPORTED for other shapes; not valid with
+ * BCONV_BINARY_WEIGHTS or BCONV_FLAG_INT8_MFMA. */
 enum {
     BCONV_FLAG_NONE = 0u,
     BCONV_FLAG_USE_BETA_SCALING = 1u,
     BCONV_FLAG_INT8_MFMA = 2u,
-    BCONV_FLAG_BETA_VALID_TAPS = 4u
+    BCONV_FLAG_BETA_VALID_TAPS = 4u,
+    BCONV_FLAG_FP4_MFMA = 8u
 };
 
 /* The activation applied last (MPSCNNBinaryConvolution, Overview, closing

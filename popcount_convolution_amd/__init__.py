@@ -16,7 +16,7 @@ import numpy as np
 
 from ._binding import (  # noqa: F401  (re-exported C ABI names)
     BCONV_AND, BCONV_BINARY_WEIGHTS, BCONV_ERR_ALLOC, BCONV_ERR_HIP, BCONV_ERR_INVALID_ARGUMENT,
-    BCONV_ERR_UNSUPPORTED, BCONV_ERR_WORKSPACE, BCONV_FLAG_BETA_VALID_TAPS, BCONV_FLAG_INT8_MFMA, BCONV_FLAG_NONE,
+    BCONV_ERR_UNSUPPORTED, BCONV_ERR_WORKSPACE, BCONV_FLAG_BETA_VALID_TAPS, BCONV_FLAG_FP4_MFMA, BCONV_FLAG_INT8_MFMA, BCONV_FLAG_NONE,
     BCONV_FLAG_USE_BETA_SCALING,
     BCONV_NEURON_NONE, BCONV_NEURON_RELU, BCONV_OK, BCONV_XNOR, NEURON_CODES, TYPE_CODES,
     BconvError, BconvLibraryMissing, bconv_calibrate_popcount, bconv_create, bconv_create_fc, bconv_desc_t,
@@ -78,7 +78,8 @@ class BinaryConvolution:
                  weight_bits: np.ndarray, output_scale=None, output_bias=None,
                  input_scale=None, input_bias=None, use_beta: bool = False,
                  neuron: str = "none", scale_value: float = 1.0, int8_mfma: bool = False,
-                 neuron_a: float = 0.0, neuron_b: float = 0.0, beta_valid_taps: bool = False):
+                 neuron_a: float = 0.0, neuron_b: float = 0.0, beta_valid_taps: bool = False,
+                 fp4_mfma: bool = False):
         pe = pad if pad_end is None else pad_end
         self.desc = make_desc(in_h, in_w, in_c, out_c, kernel[0], kernel[1], stride[0], stride[1],
                               pad[0], pad[1], 1, NEURON_CODES[neuron], scale_value, pe[0], pe[1],
@@ -86,16 +87,18 @@ class BinaryConvolution:
         self.type = TYPE_CODES[type]
         self.flags = (BCONV_FLAG_USE_BETA_SCALING if use_beta else BCONV_FLAG_NONE) | \
             (BCONV_FLAG_INT8_MFMA if int8_mfma else BCONV_FLAG_NONE) | \
-            (BCONV_FLAG_BETA_VALID_TAPS if beta_valid_taps else BCONV_FLAG_NONE)
+            (BCONV_FLAG_BETA_VALID_TAPS if beta_valid_taps else BCONV_FLAG_NONE) | \
+            (BCONV_FLAG_FP4_MFMA if fp4_mfma else BCONV_FLAG_NONE)
         self.handle = bconv_create(self.desc, weight_bits, output_scale, output_bias,
                                    input_scale, input_bias, self.type, self.flags)
         self.in_h, self.in_w = in_h, in_w
         self.in_c, self.out_c, self.out_h, self.out_w = bconv_get_info(self.handle)
 
     @classmethod
-    def from_layer(cls, layer, inputs: dict, int8_mfma: bool = False) -> "BinaryConvolution":
+    def from_layer(cls, layer, inputs: dict, int8_mfma: bool = False, fp4_mfma: bool = False) -> "BinaryConvolution":
         """Build from a ``workloads.Layer`` and the arrays ``make_inputs`` drew
-        (``int8_mfma``: the int8 matrix-core comparison path)."""
+        (``int8_mfma``: the int8 matrix-core comparison path; ``fp4_mfma``: the
+        fp4 matrix-core comparison path of fully connected layers)."""
         return cls(in_h=layer.in_h, in_w=layer.in_w, in_c=layer.in_c, out_c=layer.out_c,
                    kernel=(layer.kernel_h, layer.kernel_w), stride=(layer.stride_h, layer.stride_w),
                    pad=(layer.pad_h, layer.pad_w), pad_end=(layer.pad_h_end, layer.pad_w_end),
@@ -104,7 +107,8 @@ class BinaryConvolution:
                    output_bias=inputs.get("output_bias"), input_scale=inputs.get("input_scale"),
                    input_bias=inputs.get("input_bias"), use_beta=layer.use_beta,
                    neuron=layer.neuron, scale_value=layer.scale_value, int8_mfma=int8_mfma,
-                   neuron_a=layer.neuron_a, neuron_b=layer.neuron_b, beta_valid_taps=layer.beta_valid_taps)
+                   neuron_a=layer.neuron_a, neuron_b=layer.neuron_b, beta_valid_taps=layer.beta_valid_taps,
+                   fp4_mfma=fp4_mfma)
 
     def workspace_bytes(self, n: int) -> int:
         return bconv_workspace_size(self.handle, n)

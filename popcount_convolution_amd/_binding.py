@@ -33,6 +33,7 @@ BCONV_FLAG_NONE = 0
 BCONV_FLAG_USE_BETA_SCALING = 1
 BCONV_FLAG_INT8_MFMA = 2
 BCONV_FLAG_BETA_VALID_TAPS = 4
+BCONV_FLAG_FP4_MFMA = 8
 # bconv_neuron_t
 BCONV_NEURON_NONE = 0
 BCONV_NEURON_RELU = 1

@@ -30,8 +30,7 @@ struct bconv_handle {
     int32_t *d_lane_popc;
     uint32_t *d_flat;         // K-major weights of the fully connected route
     bool gemm;
-    void *d_f4;               // fully connected route on the fp4 matrix cores: weight table and counts
-    bool gemm_popcount;       // keep the fully connected route on the VALU popcount kernel (BCONV_GEMM_POPCOUNT)
+    void *d_f4;               // fp4 matrix-core comparison path (fully connected): weight table and counts
     bool i8;                  // int8 matrix-core comparison path (XNOR / AND)
     void *d_i8frag;           // its int8 weight fragments
     float *d_pm;              // binaryWeights, VALU kernel (+-1.0f table)
@@ -75,12 +74,17 @@ bconv_status_t check_desc(const bconv_desc_t *d, int32_t type, uint32_t flags)
     if (!d) return fail(BCONV_ERR_INVALID_ARGUMENT, "desc is NULL");
     if (type != BCONV_BINARY_WEIGHTS && type != BCONV_XNOR && type != BCONV_AND)
         return fail(BCONV_ERR_INVALID_ARGUMENT, "unknown type %d", type);
-    if (flags & ~(uint32_t)(BCONV_FLAG_USE_BETA_SCALING | BCONV_FLAG_INT8_MFMA | BCONV_FLAG_BETA_VALID_TAPS))
+    if (flags & ~(uint32_t)(BCONV_FLAG_USE_BETA_SCALING | BCONV_FLAG_INT8_MFMA | BCONV_FLAG_BETA_VALID_TAPS |
+                            BCONV_FLAG_FP4_MFMA))
         return fail(BCONV_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", flags);
     if ((flags & BCONV_FLAG_BETA_VALID_TAPS) && !(flags & BCONV_FLAG_USE_BETA_SCALING))
         return fail(BCONV_ERR_INVALID_ARGUMENT, "BCONV_FLAG_BETA_VALID_TAPS requires BCONV_FLAG_USE_BETA_SCALING");
     if ((flags & BCONV_FLAG_INT8_MFMA) && type == BCONV_BINARY_WEIGHTS)
         return fail(BCONV_ERR_INVALID_ARGUMENT, "BCONV_FLAG_INT8_MFMA applies to XNOR and AND only");
+    if ((flags & BCONV_FLAG_FP4_MFMA) && type == BCONV_BINARY_WEIGHTS)
+        return fail(BCONV_ERR_INVALID_ARGUMENT, "BCONV_FLAG_FP4_MFMA applies to XNOR and AND only");
+    if ((flags & BCONV_FLAG_FP4_MFMA) && (flags & BCONV_FLAG_INT8_MFMA))
+        return fail(BCONV_ERR_INVALID_ARGUMENT, "BCONV_FLAG_FP4_MFMA and BCONV_FLAG_INT8_MFMA exclude each other");
     if (d->neuron < 0 || d->neuron >= BCONV_NEURON_COUNT)
         return fail(BCONV_ERR_INVALID_ARGUMENT, "unknown neuron %d", d->neuron);
     if (d->groups <= 0) return fail(BCONV_ERR_INVALID_ARGUMENT, "groups must be >= 1");
@@ -414,8 +418,6 @@ bconv_status_t bconv_create(const bconv_desc_t *desc, const uint32_t *weight_bit
     h->strip_width = sp ? atoi(sp) : 0;
     const char *sf = getenv("BCONV_SMALL_FUSED");
     h->small_fused = !(sf && sf[0] == '0');
-    const char *gp = getenv("BCONV_GEMM_POPCOUNT");
-    h->gemm_popcount = gp && gp[0] == '1';
     hipError_t e = hipGetDevice(&h->device);
     int cus = 0;
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h->device);
@@ -457,6 +459,12 @@ bconv_status_t bconv_create(const bconv_desc_t *desc, const uint32_t *weight_bit
     }
 
     const bconv::Geom g = make_geom(h, 1);
+    if ((flags & BCONV_FLAG_FP4_MFMA) && !bconv::gemm_f4_route(g)) {
+        (void)hipFree(d_user);
+        release(h);
+        return fail(BCONV_ERR_UNSUPPORTED, "BCONV_FLAG_FP4_MFMA needs the fully connected shape with a window of a "
+                                           "multiple of 4 words (kernel_h*kernel_w*ceil(in_c/32) %% 4 == 0)");
+    }
     if (type != BCONV_BINARY_WEIGHTS) {
         h->lane.kwc4 = (desc->kernel_w * h->words + 3) / 4;
         const size_t nw = (size_t)h->tiles * desc->kernel_h * h->lane.kwc4 * 256;
@@ -492,7 +500,7 @@ bconv_status_t bconv_create(const bconv_desc_t *desc, const uint32_t *weight_bit
         e = hipMalloc(reinterpret_cast<void **>(&h->d_flat), bconv::gemm_weight_words(g) * 4);
         if (e == hipSuccess) e = bconv::launch_prepack_flat(g, nullptr, d_user, h->d_flat);
     }
-    if (e == hipSuccess && h->gemm && !h->i8 && !h->gemm_popcount && bconv::gemm_f4_route(g)) {
+    if (e == hipSuccess && (flags & BCONV_FLAG_FP4_MFMA)) {
         e = hipMalloc(&h->d_f4, bconv::gemm_f4_bytes(g));
         if (e == hipSuccess) e = bconv::launch_prepack_f4(g, nullptr, d_user, h->d_f4);
     }

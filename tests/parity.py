@@ -29,18 +29,15 @@ TINY = 1e-30
 
 
 @contextmanager
-def force_generic(on: bool, strip_width: int = 0, small_fused=None, gemm_popcount: bool = False):
+def force_generic(on: bool, strip_width: int = 0, small_fused=None):
     """Handles created inside use the generic convolution kernel, or the
     specialised one at the given strip width (0: chosen by cost).  Small
     layers take the single-launch kernel by default; a forced kernel or
-    strip width, or small_fused=False, keeps them on the two-kernel path.
-    ``gemm_popcount`` keeps fully connected layers on the VALU popcount
-    product instead of the fp4 matrix-core one."""
+    strip width, or small_fused=False, keeps them on the two-kernel path."""
     if small_fused is None:
         small_fused = not on and not strip_width
     values = {"BCONV_FORCE_GENERIC": "1" if on else "0", "BCONV_STRIP_WIDTH": str(strip_width),
-              "BCONV_SMALL_FUSED": "1" if small_fused else "0",
-              "BCONV_GEMM_POPCOUNT": "1" if gemm_popcount else "0"}
+              "BCONV_SMALL_FUSED": "1" if small_fused else "0"}
     old = {k: os.environ.get(k) for k in values}
     os.environ.update(values)
     try:
@@ -60,16 +57,17 @@ def slice_inputs(inputs: dict, images) -> dict:
 
 
 def run_gpu(layer: workloads.Layer, inputs: dict, device, generic: bool = False,
-            int8_mfma: bool = False, strip_width: int = 0, small_fused=None, gemm_popcount: bool = False) -> dict:
+            int8_mfma: bool = False, strip_width: int = 0, small_fused=None, fp4_mfma: bool = False) -> dict:
     """Forward and forward_accum through the C ABI; also returns the
     workspace intermediates (bits or int8 values, A map, beta) of the forward
     call.  ``int8_mfma`` selects the int8 matrix-core comparison path;
     ``strip_width`` forces the specialised convolution's pixels per wave;
     ``small_fused`` (None: the library's default) selects or avoids the
     single-launch small-layer kernel, which writes no workspace intermediates;
-    ``gemm_popcount`` keeps a fully connected layer on the VALU popcount GEMM."""
-    with force_generic(generic, strip_width, small_fused, gemm_popcount):
-        conv = pca.BinaryConvolution.from_layer(layer, inputs, int8_mfma=int8_mfma)
+    ``fp4_mfma`` selects the fp4 matrix-core comparison path of a fully
+    connected layer."""
+    with force_generic(generic, strip_width, small_fused):
+        conv = pca.BinaryConvolution.from_layer(layer, inputs, int8_mfma=int8_mfma, fp4_mfma=fp4_mfma)
     try:
         n = inputs["x"].shape[0]
         x = torch.from_numpy(inputs["x"]).to(device)

@@ -60,7 +60,10 @@ def _desc(**kw):
     ({}, pca.BCONV_XNOR, pca.BCONV_FLAG_BETA_VALID_TAPS, pca.BCONV_ERR_INVALID_ARGUMENT),
     ({}, pca.BCONV_XNOR, pca.BCONV_FLAG_BETA_VALID_TAPS | pca.BCONV_FLAG_USE_BETA_SCALING, pca.BCONV_OK),
     ({}, pca.BCONV_BINARY_WEIGHTS, pca.BCONV_FLAG_BETA_VALID_TAPS | pca.BCONV_FLAG_USE_BETA_SCALING, pca.BCONV_OK),
-    ({}, pca.BCONV_AND, 8, pca.BCONV_ERR_INVALID_ARGUMENT),
+    ({}, pca.BCONV_AND, 16, pca.BCONV_ERR_INVALID_ARGUMENT),
+    ({}, pca.BCONV_XNOR, pca.BCONV_FLAG_FP4_MFMA, pca.BCONV_OK),  # the shape is checked by bconv_create
+    ({}, pca.BCONV_BINARY_WEIGHTS, pca.BCONV_FLAG_FP4_MFMA, pca.BCONV_ERR_INVALID_ARGUMENT),
+    ({}, pca.BCONV_AND, pca.BCONV_FLAG_FP4_MFMA | pca.BCONV_FLAG_INT8_MFMA, pca.BCONV_ERR_INVALID_ARGUMENT),
     ({}, pca.BCONV_XNOR, 4, pca.BCONV_ERR_INVALID_ARGUMENT),
     (dict(neuron=11, neuron_a=-1.0, neuron_b=1.0), pca.BCONV_XNOR, 0, pca.BCONV_OK),  # clamp
     (dict(neuron=12), pca.BCONV_XNOR, 0, pca.BCONV_ERR_INVALID_ARGUMENT),

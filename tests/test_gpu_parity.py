@@ -436,9 +436,9 @@ def _bits_layers():
 BITS_LAYERS = _bits_layers()
 
 
-def _run_bits(layer, inputs, dev, generic=False, int8=False):
+def _run_bits(layer, inputs, dev, generic=False, int8=False, fp4=False):
     with parity.force_generic(generic):
-        conv = pca.BinaryConvolution.from_layer(layer, inputs, int8_mfma=int8)
+        conv = pca.BinaryConvolution.from_layer(layer, inputs, int8_mfma=int8, fp4_mfma=fp4)
     try:
         x = torch.from_numpy(inputs["x"]).to(dev)
         words = conv.forward_bits(x).cpu().numpy()
@@ -505,13 +505,13 @@ def _packed_layers():
 PACKED_LAYERS = _packed_layers()
 
 
-def _packed_run(layer, inputs, words, dev, generic=False):
+def _packed_run(layer, inputs, words, dev, generic=False, fp4=False):
     """forward_packed (fp32 and bits) of `words` on a workspace poisoned with
     0xA5, and forward / forward_accum of the +-1 values the words stand for, on
     one handle.  Also returns the padded bit buffer the repad kernel wrote."""
     values = parity.values_from_bits(words, layer.in_c)
     with parity.force_generic(generic):
-        conv = pca.BinaryConvolution.from_layer(layer, inputs)
+        conv = pca.BinaryConvolution.from_layer(layer, inputs, fp4_mfma=fp4)
     try:
         n = words.shape[0]
         w = torch.from_numpy(words.view(np.int32)).to(dev)
@@ -1051,30 +1051,54 @@ FC_F4 = _fc_f4_layers()
 
 @pytest.mark.parametrize("layer", FC_F4, ids=[l.name for l in FC_F4])
 def test_fc_fp4_route(dev, layer):
-    """The fully connected product on the fp4 matrix cores: fp32 output and
-    window sums compared with the oracle on every output; window sums and fp32
-    outputs identical to the VALU popcount GEMM's; sign-bit output; and
-    (without beta / affine) packed input."""
+    """The fully connected product on the fp4 matrix cores
+    (BCONV_FLAG_FP4_MFMA): fp32 output and window sums compared with the
+    oracle on every output; window sums and fp32 outputs identical to the VALU
+    popcount GEMM's; sign-bit output; and (without beta / affine) packed
+    input."""
     assert layer.is_fc
     seed = 9400 + FC_F4.index(layer)
     inputs = workloads.make_inputs(layer, seed)
     _log(f"fc fp4 {layer} seed {seed}")
     ref = oracle.bconv_layer(layer, inputs)
-    got = parity.run_gpu(layer, inputs, dev)
+    got = parity.run_gpu(layer, inputs, dev, fp4_mfma=True)
     assert got["main_kernel"].startswith("bgemm_f4_kernel"), got["main_kernel"]
     parity.compare(layer, inputs, got, ref=ref)
-    pop = parity.run_gpu(layer, inputs, dev, gemm_popcount=True)
+    pop = parity.run_gpu(layer, inputs, dev)
     assert pop["main_kernel"].startswith("bgemm_kernel"), pop["main_kernel"]
     assert np.array_equal(got["acc"], pop["acc"])
     assert np.array_equal(got["out"].view(np.uint32), pop["out"].view(np.uint32))
-    words, out, kernel = _run_bits(layer, inputs, dev)
+    words, out, kernel = _run_bits(layer, inputs, dev, fp4=True)
     assert kernel.startswith("bgemm_f4_kernel"), kernel
     assert np.array_equal(parity.unpack_words(words, layer.out_c), (~(out < 0)).astype(np.uint8)), kernel
     assert not parity.unpack_words(words, None)[..., layer.out_c:].any(), "output bits past out_c are set"
     parity.compare_bits(layer, inputs, words, ref=ref)
     if not layer.use_beta:
         pw = workloads.make_packed_input(layer, 9500 + FC_F4.index(layer))
-        _check_packed(layer, inputs, pw, _packed_run(layer, inputs, pw, dev))
+        r = _packed_run(layer, inputs, pw, dev, fp4=True)
+        assert r["kernel"].startswith("bgemm_f4_kernel"), r["kernel"]
+        _check_packed(layer, inputs, pw, r)
+
+
+def test_fc_fp4_measured_layer_full(dev):
+    """The measured fully connected layer (256 x 7x7x512 -> 4096) on the fp4
+    matrix cores at full size, every output compared with the oracle."""
+    index = next(i for i, l in enumerate(workloads.LAYERS) if l.is_fc)
+    layer = workloads.LAYERS[index]
+    inputs, ref = measured_reference(index)
+    got = parity.run_gpu(layer, inputs, dev, fp4_mfma=True)
+    assert got["main_kernel"].startswith("bgemm_f4_kernel"), got["main_kernel"]
+    parity.compare(layer, inputs, got, ref=ref)
+
+
+def test_fc_fp4_unsupported_shapes(dev):
+    """BCONV_FLAG_FP4_MFMA on a convolution, or on a fully connected window
+    that is not a multiple of 4 words, is refused at creation."""
+    for layer in (workloads.BENCH_LAYER.with_(n=1), FC_TAIL[0]):
+        inputs = workloads.make_inputs(layer, 9600)
+        with pytest.raises(pca.BconvError) as e:
+            pca.BinaryConvolution.from_layer(layer, inputs, fp4_mfma=True)
+        assert e.value.status == pca.BCONV_ERR_UNSUPPORTED, layer.name
 
 
 @pytest.mark.parametrize("layer", FC_TAIL[:4], ids=[l.name for l in FC_TAIL[:4]])
