@@ -232,72 +232,79 @@ __global__ __launch_bounds__(64 * kF4Waves) void bgemm_f4_kernel(const uint4 *bi
     }
     __syncthreads();
 
-    // epilogue: wave w finishes row fragment w / 2, channel fragments
-    // 2 (w % 2) and 2 (w % 2) + 1; lane = column r16 of rows 4 kq .. 4 kq + 3
-    const int f = wave >> 1;
-    const int rbase = 16 * f + 4 * kq;  // first of the lane's 4 rows in the block
-    uint4 sx = make_uint4(0u, 0u, 0u, 0u);
-    if (!AND) {
+    // epilogue, by pairs of channel fragments: pair q is row fragment q / 2
+    // with channel fragments 2 (q % 2) and 2 (q % 2) + 1, i.e. 32 channels =
+    // one output sign-bit word; wave w takes pairs w * kPairs ... ; lane =
+    // column r16 of rows 4 kq .. 4 kq + 3 of the fragment
+    constexpr int kPairs = 8 / kF4Waves;
 #pragma unroll
-        for (int w = 0; w < kF4Waves; ++w) {
-            const uint4 p = rowpart[w][rbase / 4];
-            sx.x += p.x;
-            sx.y += p.y;
-            sx.z += p.z;
-            sx.w += p.w;
-        }
-    }
-    const uint32_t sxr[4] = {sx.x, sx.y, sx.z, sx.w};
-    float be[4] = {1.0f, 1.0f, 1.0f, 1.0f};
-    if (a.a_pad) {
+    for (int pi = 0; pi < kPairs; ++pi) {
+        const int q = wave * kPairs + pi;
+        const int f = q >> 1;
+        const int rbase = 16 * f + 4 * kq;  // first of the lane's 4 rows in the block
+        uint4 sx = make_uint4(0u, 0u, 0u, 0u);
+        if (!AND) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) be[j] = rbeta[rbase + j];
-    }
-    bool bit[2][4];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int g = 2 * (wave & 1) + h;
-        v4f s = part[0][f * 4 + g][lane];
-#pragma unroll
-        for (int w = 1; w < kF4Waves; ++w) s += part[w][f * 4 + g][lane];
-        const int co = tile * kTile + 16 * g + r16;
-        const bool co_ok = co < a.out_c;
-        const int sw = co_ok && !AND ? a.wcount[co] : 0;
-        const float sc = a.scale ? (co_ok ? a.scale[co] : 0.0f) : a.scale_value;
-        const float bi = a.bias ? (co_ok ? a.bias[co] : 0.0f) : 0.0f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int m = m0 + rbase + j;
-            const int sxw = (int)s[j];  // exact: an integer below 2^24
-            const int v = AND ? sxw : a.kbits - 2 * ((int)sxr[j] + sw - 2 * sxw);
-            bit[h][j] = false;
-            if (m >= n || !co_ok) continue;
-            const long long o = (long long)m * a.out_c + co;
-            if (a.acc_out) {
-                store_through(&a.acc_out[o], v);
-                continue;
+            for (int w = 0; w < kF4Waves; ++w) {
+                const uint4 p = rowpart[w][rbase / 4];
+                sx.x += p.x;
+                sx.y += p.y;
+                sx.z += p.z;
+                sx.w += p.w;
             }
-            const float res = epilogue_value((float)v, sc, be[j], bi, a.neuron);
-            if (a.bits_out) {
-                bit[h][j] = sign_bit(res);
-                continue;
-            }
-            store_through(&a.out[o], res);
         }
-    }
-    if (a.bits_out) {
-        // the wave's 32 channels are output word 2 * tile + (wave & 1) of each
-        // row: low half from channel fragment 0, high half from fragment 1
-        const int wi = 2 * tile + (wave & 1);
+        const uint32_t sxr[4] = {sx.x, sx.y, sx.z, sx.w};
+        float be[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+        if (a.a_pad) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const unsigned long long lo = __ballot(bit[0][j]), hi = __ballot(bit[1][j]);
-            // lane q < 4 writes row 4q + j of the fragment
-            if (lane < 4 && wi < a.out_words) {
-                const int m = m0 + 16 * f + 4 * lane + j;
-                const uint32_t word = (uint32_t)((lo >> (16 * lane)) & 0xffffu) |
-                                      ((uint32_t)((hi >> (16 * lane)) & 0xffffu) << 16);
-                if (m < n) store_through(&a.bits_out[(long long)m * a.out_words + wi], word);
+            for (int j = 0; j < 4; ++j) be[j] = rbeta[rbase + j];
+        }
+        bool bit[2][4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int g = 2 * (q & 1) + h;
+            v4f s = part[0][f * 4 + g][lane];
+#pragma unroll
+            for (int w = 1; w < kF4Waves; ++w) s += part[w][f * 4 + g][lane];
+            const int co = tile * kTile + 16 * g + r16;
+            const bool co_ok = co < a.out_c;
+            const int sw = co_ok && !AND ? a.wcount[co] : 0;
+            const float sc = a.scale ? (co_ok ? a.scale[co] : 0.0f) : a.scale_value;
+            const float bi = a.bias ? (co_ok ? a.bias[co] : 0.0f) : 0.0f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int m = m0 + rbase + j;
+                const int sxw = (int)s[j];  // exact: an integer below 2^24
+                const int v = AND ? sxw : a.kbits - 2 * ((int)sxr[j] + sw - 2 * sxw);
+                bit[h][j] = false;
+                if (m >= n || !co_ok) continue;
+                const long long o = (long long)m * a.out_c + co;
+                if (a.acc_out) {
+                    store_through(&a.acc_out[o], v);
+                    continue;
+                }
+                const float res = epilogue_value((float)v, sc, be[j], bi, a.neuron);
+                if (a.bits_out) {
+                    bit[h][j] = sign_bit(res);
+                    continue;
+                }
+                store_through(&a.out[o], res);
+            }
+        }
+        if (a.bits_out) {
+            // output word 2 * tile + (q & 1) of each row: low half from the
+            // pair's first channel fragment, high half from its second
+            const int wi = 2 * tile + (q & 1);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const unsigned long long lo = __ballot(bit[0][j]), hi = __ballot(bit[1][j]);
+                // lane c < 4 writes row 4c + j of the fragment
+                if (lane < 4 && wi < a.out_words) {
+                    const int m = m0 + 16 * f + 4 * lane + j;
+                    const uint32_t word = (uint32_t)((lo >> (16 * lane)) & 0xffffu) |
+                                          ((uint32_t)((hi >> (16 * lane)) & 0xffffu) << 16);
+                    if (m < n) store_through(&a.bits_out[(long long)m * a.out_words + wi], word);
+                }
             }
         }
     }
