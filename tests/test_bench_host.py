@@ -57,6 +57,7 @@ def test_kernel_source_hash(tmp_path, monkeypatch):
     monkeypatch.undo()
     assert a == bench._kernel_sha("xconv_fast<3,3,8,1,7>")  # same source file
     assert a != bench._kernel_sha("bgemm_kernel<false>")
+    assert bench._kernel_sha("bgemm_f4_kernel<false>") != bench._kernel_sha("bgemm_kernel<false>")
     assert bench.recorded_traffic("no such workload", "xconv_fast<3,3,4,1,7>") is None
     assert bench.recorded_traffic(workloads.BENCH_LAYER.name, "bgemm_kernel<false>") is None
 
@@ -79,3 +80,18 @@ def test_headline_is_the_largest_layer():
     """The default line quotes the layer with the most bit-MACs per step."""
     biggest = max(workloads.LAYERS, key=lambda l: l.nominal_macs())
     assert workloads.HEADLINE_LAYER is biggest and biggest.is_fc
+
+
+def test_fp4_route_and_roofline():
+    """The fp4 comparison path takes the fully connected XNOR / AND layers
+    whose window is a multiple of 4 words; its roofline counts two fp4
+    operations per bit-MAC against the dense fp4 peak."""
+    L = workloads.LAYERS
+    assert [bench.fp4_route(l) for l in L] == [False, False, False, False, True]
+    assert not bench.fp4_route(L[4].with_(in_c=96))       # 7*7*3 = 147 words
+    assert not bench.fp4_route(L[4].with_(type="binary_weights"))
+    r = bench.fp4_roofline(L[4], 256, 0.010)             # 10 us per launch
+    macs = 256 * 4096 * 7 * 7 * 512
+    assert r["bound"] == "mfma" and r["peak"] == 10100.0
+    assert abs(r["achieved"] - 2 * macs / 1e-5 / 1e12) < 1e-2
+    assert abs(r["of_popcount_peak"] - macs / 1e-5 / 1e12 / bench.POPCOUNT_PEAK_TBITMAC) < 1e-4
