@@ -288,9 +288,15 @@ def roofline_of(layer, n, kernel_ms, bits_out=False, kernel=""):
 
 def fp4_route(layer):
     """Whether the fp4 matrix-core comparison path takes the layer: XNOR / AND
-    of the fully connected shape with a window of a multiple of 4 words."""
-    return (layer.type != "binary_weights" and layer.is_fc
-            and (layer.kernel_h * layer.kernel_w * ((layer.in_c + 31) // 32)) % 4 == 0)
+    of the fully connected shape with a window of a multiple of 4 words, or a
+    convolution whose pixel is a multiple of 4 words (at most 1024 groups of
+    4 words per window)."""
+    if layer.type == "binary_weights":
+        return False
+    words = (layer.in_c + 31) // 32
+    if layer.is_fc:
+        return (layer.kernel_h * layer.kernel_w * words) % 4 == 0
+    return words % 4 == 0 and layer.kernel_h * layer.kernel_w * words // 4 <= 1024
 
 
 def fp4_roofline(layer, n, kernel_ms):
@@ -389,15 +395,15 @@ def measure_layer(pca, torch, np, workloads, index, args, stream):
                          "frac": round(r8[1] / r8[2], 4), "algorithmic_bytes": nb8,
                          "traffic": recorded_traffic(layer.name + "#int8_mfma", k8)}}
         conv8.close()
-    if binary and not args.no_int8 and fp4_route(layer):
+    if not args.no_int8 and fp4_route(layer):
         conv4 = pca.BinaryConvolution.from_layer(layer, inputs, fp4_mfma=True)
         ms4, main4, _, out4 = time_path(pca, torch, np, conv4, n, x, stream, args.warmup, args.steps)
         same4 = bool(torch.equal(out4, out))
         del out4
         k4 = conv4.main_kernel(n)
         comparison["fp4_mfma"] = {
-            "what": "the fully connected product on the fp4 matrix cores (BCONV_FLAG_FP4_MFMA): the 0/1 bit "
-                    "product count as exact e2m1 products, XNOR from it and the input and weight bit counts",
+            "what": "the layer on the fp4 matrix cores (BCONV_FLAG_FP4_MFMA): the 0/1 bit product count as exact "
+                    "e2m1 products, XNOR from it and the input and weight bit counts",
             "value": round(macs / (ms4 / 1e3) / 1e9, 3), "unit": unit,
             "ms_per_step": round(ms4, 6), "kernel": k4, "avg_kernel_us": round(main4 * 1e3, 3),
             "kernel_speed_vs_popcount": round(main_ms / main4, 4),

@@ -98,15 +98,18 @@ typedef enum {
  * divisor of the page's first beta equation where the window leaves the
  * image; identical inside the image).  Requires BCONV_FLAG_USE_BETA_SCALING.
  * BCONV_FLAG_FP4_MFMA selects a second comparison path, on the fp4 matrix
- * cores, for XNOR and AND layers of the fully connected shape
- * (MPSCNNFullyConnected, Overview, conditions) whose window holds a multiple
- * of 4 words (kernel_h * kernel_w * ceil(in_c / 32) % 4 == 0): the product
- * count of the 0/1 bits, sum_k x_k * w_k, runs as exact e2m1 products with
- * fp32 accumulation; AND is that count and XNOR follows from it and the
- * counts of set input and weight bits (popcount(x ^ w) = S_x + S_w - 2 S_xw).
- * Results are identical (exact integers, the same fp32 epilogue); the
- * workspace is that of the popcount path.  bconv_create returns
- * BCONV_ERR_UNSUPPORTED for other shapes; not valid with
+ * cores, for XNOR and AND layers: the product count of the 0/1 bits,
+ * sum_k x_k * w_k, runs as exact e2m1 products with fp32 accumulation; AND
+ * is that count and XNOR follows from it and the counts of set input and
+ * weight bits over the window's in-image taps (popcount(x ^ w) = S_x + S_w -
+ * 2 S_xw).  It takes layers of the fully connected shape (MPSCNNFullyConnected,
+ * Overview, conditions) whose window holds a multiple of 4 words
+ * (kernel_h * kernel_w * ceil(in_c / 32) % 4 == 0), and convolutions whose
+ * pixel holds a multiple of 4 words (ceil(in_c / 32) % 4 == 0) with at most
+ * 4096 words per window; the padded bit buffer must stay below 2 GiB per
+ * call (else BCONV_ERR_HIP).  Results are identical (exact integers, the same
+ * fp32 epilogue); the workspace is that of the popcount path.  bconv_create
+ * returns BCONV_ERR_UNSUPPORTED for other shapes; not valid with
  * BCONV_BINARY_WEIGHTS or BCONV_FLAG_INT8_MFMA. */
 enum {
     BCONV_FLAG_NONE = 0u,

@@ -30,7 +30,7 @@ struct bconv_handle {
     int32_t *d_lane_popc;
     uint32_t *d_flat;         // K-major weights of the fully connected route
     bool gemm;
-    void *d_f4;               // fp4 matrix-core comparison path (fully connected): weight table and counts
+    void *d_f4;               // fp4 matrix-core comparison path: weight table and set-bit counts
     bool i8;                  // int8 matrix-core comparison path (XNOR / AND)
     void *d_i8frag;           // its int8 weight fragments
     float *d_pm;              // binaryWeights, VALU kernel (+-1.0f table)
@@ -227,7 +227,8 @@ bool ranges_overlap(const void *a, size_t an, const void *b, size_t bn)
 // Whether a call with fp32 input takes the single-launch small-layer kernel.
 bool takes_small(const bconv_handle *h, const bconv::Geom &g)
 {
-    return h->small_fused && !h->force_generic && !h->i8 && h->type != BCONV_BINARY_WEIGHTS && !uses_beta(h) &&
+    return h->small_fused && !h->force_generic && !h->i8 && !h->d_f4 && h->type != BCONV_BINARY_WEIGHTS &&
+           !uses_beta(h) &&
            bconv::small_route(g);
 }
 
@@ -337,10 +338,10 @@ bconv_status_t forward_impl(bconv_t h, void *stream, int32_t n, const void *src,
         e = bconv::launch_bwconv(g, main, in, h->d_in_scale, h->d_in_bias, h->d_pm, h->pm_cols, ep,
                                  sink == Sink::Output ? static_cast<float *>(dst) : nullptr,
                                  sink == Sink::Accum ? static_cast<float *>(dst) : nullptr);
-    } else if (h->gemm && !h->force_generic && h->d_f4) {
-        e = bconv::launch_gemm_f4(g, main, h->type == BCONV_AND, bits, h->d_f4, ep,
-                                  sink == Sink::Output ? static_cast<float *>(dst) : nullptr,
-                                  sink == Sink::Accum ? static_cast<int32_t *>(dst) : nullptr);
+    } else if (h->d_f4 && !h->force_generic) {
+        e = bconv::launch_f4(g, main, h->type == BCONV_AND, bits, h->d_f4, ep,
+                             sink == Sink::Output ? static_cast<float *>(dst) : nullptr,
+                             sink == Sink::Accum ? static_cast<int32_t *>(dst) : nullptr);
     } else if (h->gemm && !h->force_generic) {
         e = bconv::launch_gemm(g, main, h->type == BCONV_AND, bits, h->d_flat, ep,
                                sink == Sink::Output ? static_cast<float *>(dst) : nullptr,
@@ -459,11 +460,12 @@ bconv_status_t bconv_create(const bconv_desc_t *desc, const uint32_t *weight_bit
     }
 
     const bconv::Geom g = make_geom(h, 1);
-    if ((flags & BCONV_FLAG_FP4_MFMA) && !bconv::gemm_f4_route(g)) {
+    if ((flags & BCONV_FLAG_FP4_MFMA) && !bconv::f4_route(g)) {
         (void)hipFree(d_user);
         release(h);
-        return fail(BCONV_ERR_UNSUPPORTED, "BCONV_FLAG_FP4_MFMA needs the fully connected shape with a window of a "
-                                           "multiple of 4 words (kernel_h*kernel_w*ceil(in_c/32) %% 4 == 0)");
+        return fail(BCONV_ERR_UNSUPPORTED,
+                    "BCONV_FLAG_FP4_MFMA needs a fully connected window of a multiple of 4 words, or a convolution "
+                    "with ceil(in_c/32) a multiple of 4 and at most 4096 words per window");
     }
     if (type != BCONV_BINARY_WEIGHTS) {
         h->lane.kwc4 = (desc->kernel_w * h->words + 3) / 4;
@@ -501,7 +503,7 @@ bconv_status_t bconv_create(const bconv_desc_t *desc, const uint32_t *weight_bit
         if (e == hipSuccess) e = bconv::launch_prepack_flat(g, nullptr, d_user, h->d_flat);
     }
     if (e == hipSuccess && (flags & BCONV_FLAG_FP4_MFMA)) {
-        e = hipMalloc(&h->d_f4, bconv::gemm_f4_bytes(g));
+        e = hipMalloc(&h->d_f4, bconv::f4_bytes(g));
         if (e == hipSuccess) e = bconv::launch_prepack_f4(g, nullptr, d_user, h->d_f4);
     }
     if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
@@ -654,7 +656,7 @@ const char *bconv_main_kernel(bconv_t h, int32_t n)
         return h->force_generic ? bconv::bwconv_kernel_name(g) : bconv::bwmma_kernel_name(g, h->d_in_scale != nullptr);
     if (h->force_generic) return "xconv_generic";
     if (takes_small(h, g)) return bconv::small_kernel_name(g, h->type == BCONV_AND);
-    if (h->gemm && h->d_f4) return bconv::gemm_f4_kernel_name(h->type == BCONV_AND);
+    if (h->d_f4) return bconv::f4_kernel_name(g, h->type == BCONV_AND);
     if (h->gemm) return bconv::gemm_kernel_name(g, h->type == BCONV_AND);
     return bconv::xconv_kernel_name(g);
 }

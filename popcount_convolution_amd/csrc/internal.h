@@ -80,6 +80,24 @@ __device__ __forceinline__ float epilogue_value(float v, float sc, float be, flo
     return apply_neuron(n, __builtin_fmaf(v * sc, be, bi));
 }
 
+// apply_neuron as one out-of-line copy per translation unit.
+static __device__ __attribute__((noinline)) float apply_neuron_outline(int type, float na, float nb, float r)
+{
+    return apply_neuron(Neuron{type, na, nb}, r);
+}
+
+// epilogue_value for kernels that form many values per lane: identity and
+// ReLU inline, every other neuron through the one out-of-line copy (the whole
+// switch inlined at each value would overflow the instruction cache).  The
+// same arithmetic, so the same results.
+__device__ __forceinline__ float epilogue_value_compact(float v, float sc, float be, float bi, const Neuron &n)
+{
+    const float r = __builtin_fmaf(v * sc, be, bi);
+    if (n.type == kNeuronNone) return r;
+    if (n.type == kNeuronRelu) return (r < 0.0f) ? 0.0f : r;
+    return apply_neuron_outline(n.type, n.a, n.b, r);
+}
+
 // Sign bit of an output value, in the input encoding of the next binary
 // layer: 1 unless y < 0 (so +-0 and NaN give 1).
 __device__ __forceinline__ bool sign_bit(float y) { return !(y < 0.0f); }
@@ -225,14 +243,15 @@ hipError_t launch_prepack_flat(const Geom &g, hipStream_t s, const uint32_t *use
 const char *gemm_kernel_name(const Geom &g, int and_mode);
 hipError_t launch_gemm(const Geom &g, const Launch &L, int and_mode, const uint32_t *bits, const uint32_t *wflat,
                        const Epilogue &e, float *out, int32_t *acc_out);
-// The same product on the fp4 matrix cores (0/1 bit counts, exact in fp32):
-// taken when the row length in words is a multiple of 4.
-bool gemm_f4_route(const Geom &g);
-size_t gemm_f4_bytes(const Geom &g);
+// XNOR / AND on the fp4 matrix cores (comparison path; 0/1 bit counts, exact
+// in fp32): the fully connected product when its row is a multiple of 4
+// words, a convolution when a pixel is (at most 1024 word groups per window).
+bool f4_route(const Geom &g);
+size_t f4_bytes(const Geom &g);
 hipError_t launch_prepack_f4(const Geom &g, hipStream_t s, const uint32_t *user_bits, void *tab);
-const char *gemm_f4_kernel_name(int and_mode);
-hipError_t launch_gemm_f4(const Geom &g, const Launch &L, int and_mode, const uint32_t *bits, const void *tab,
-                          const Epilogue &e, float *out, int32_t *acc_out);
+const char *f4_kernel_name(const Geom &g, int and_mode);
+hipError_t launch_f4(const Geom &g, const Launch &L, int and_mode, const uint32_t *bits, const void *tab,
+                     const Epilogue &e, float *out, int32_t *acc_out);
 hipError_t launch_bwconv(const Geom &g, const Launch &L, const float *x, const float *in_scale,
                          const float *in_bias, const float *pm_weights, int pm_cols,
                          const Epilogue &e, float *out, float *acc_out);

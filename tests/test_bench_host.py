@@ -83,11 +83,13 @@ def test_headline_is_the_largest_layer():
 
 
 def test_fp4_route_and_roofline():
-    """The fp4 comparison path takes the fully connected XNOR / AND layers
-    whose window is a multiple of 4 words; its roofline counts two fp4
-    operations per bit-MAC against the dense fp4 peak."""
+    """The fp4 comparison path takes XNOR / AND layers whose fully connected
+    window, or convolution pixel, is a multiple of 4 words; its roofline
+    counts two fp4 operations per bit-MAC against the dense fp4 peak, or HBM
+    where the layer's bytes take longer."""
     L = workloads.LAYERS
-    assert [bench.fp4_route(l) for l in L] == [False, False, False, False, True]
+    assert [bench.fp4_route(l) for l in L] == [False, True, True, False, True]
+    assert bench.fp4_roofline(L[1], 8, 0.005)["bound"] == "hbm"
     assert not bench.fp4_route(L[4].with_(in_c=96))       # 7*7*3 = 147 words
     assert not bench.fp4_route(L[4].with_(type="binary_weights"))
     r = bench.fp4_roofline(L[4], 256, 0.010)             # 10 us per launch

@@ -1032,6 +1032,7 @@ def _fc_f4_layers():
         dict(in_h=4, in_w=4, in_c=100, out_c=1, n=3),      # 4 bits of the last word valid
         dict(in_h=1, in_w=2, in_c=255, out_c=64, n=1),     # one row
         dict(in_h=5, in_w=5, in_c=128, out_c=200, n=40),   # K = 100: 6 steps + 1 word group
+        dict(in_h=2, in_w=2, in_c=256, out_c=70, n=20, neuron="sigmoid"),
     ]
     out = []
     for gi, g in enumerate(geoms):
@@ -1091,10 +1092,81 @@ def test_fc_fp4_measured_layer_full(dev):
     parity.compare(layer, inputs, got, ref=ref)
 
 
+def _conv_f4_layers():
+    """Convolutions the fp4 matrix-core comparison path takes (a pixel of a
+    multiple of 4 words): the XNOR + beta + affine + ReLU form, AND, several
+    channel tiles, 5x5 and 7x7 windows (196 word groups), stride 2 without
+    padding, a 1x1 window, an even window with the centred padding, and
+    channels that leave tail bits in a pixel's last word."""
+    base = workloads.Layer("conv_f4", "xnor", 2, 9, 10, 128, 70, 3, 3, 1, 1, 1, 1)
+    geoms = [
+        dict(use_beta=True, neuron="relu", iscale_dist=("uniform", 0.5, 1.5), ibias_dist=("normal", 0.0, 0.2)),
+        dict(type="and"),
+        dict(),
+        dict(n=1, in_h=12, in_w=11, in_c=256, out_c=130, kernel_h=5, kernel_w=5, pad_h=2, pad_w=2, type="and"),
+        dict(n=1, in_h=12, in_w=11, in_c=256, out_c=130, kernel_h=5, kernel_w=5, pad_h=2, pad_w=2),
+        dict(n=3, in_h=13, in_w=9, out_c=64, stride_h=2, stride_w=2, pad_h=0, pad_w=0),
+        dict(n=2, in_h=8, in_w=8, in_c=512, out_c=33, kernel_h=1, kernel_w=1, pad_h=0, pad_w=0),
+        dict(n=2, in_h=7, in_w=8, out_c=20, kernel_h=2, kernel_w=2, pad_h=1, pad_w=1, pad_bottom=0, pad_right=0,
+             use_beta=True),
+        dict(in_c=100, out_c=17),
+        dict(in_c=100, out_c=17, type="and"),
+        dict(n=1, in_h=10, in_w=10, in_c=512, out_c=16, kernel_h=7, kernel_w=7, pad_h=3, pad_w=3),
+        dict(neuron="tanh", neuron_a=1.5, neuron_b=0.5, use_beta=True),   # neurons outside the inline pair
+        dict(neuron="elu", neuron_a=0.7, type="and"),
+    ]
+    return [base.with_(**dict(g, name=f"conv_f4_{i}")) for i, g in enumerate(geoms)]
+
+
+CONV_F4 = _conv_f4_layers()
+
+
+@pytest.mark.parametrize("layer", CONV_F4, ids=[l.name for l in CONV_F4])
+def test_conv_fp4_route(dev, layer):
+    """Convolutions on the fp4 matrix cores (BCONV_FLAG_FP4_MFMA): every output
+    compared with the oracle; window sums identical to the popcount path's and
+    fp32 outputs to the generic kernel's (same beta summation order); sign-bit
+    output; and (without beta / affine) packed input."""
+    assert not layer.is_fc
+    seed = 9700 + CONV_F4.index(layer)
+    inputs = workloads.make_inputs(layer, seed)
+    _log(f"conv fp4 {layer} seed {seed}")
+    ref = oracle.bconv_layer(layer, inputs)
+    got = parity.run_gpu(layer, inputs, dev, fp4_mfma=True)
+    assert got["main_kernel"].startswith("xconv_f4_kernel"), got["main_kernel"]
+    parity.compare(layer, inputs, got, ref=ref)
+    pop = parity.run_gpu(layer, inputs, dev)
+    assert np.array_equal(got["acc"], pop["acc"]), pop["main_kernel"]
+    gen = parity.run_gpu(layer, inputs, dev, generic=True)
+    assert np.array_equal(got["out"].view(np.uint32), gen["out"].view(np.uint32))
+    words, out, kernel = _run_bits(layer, inputs, dev, fp4=True)
+    assert kernel.startswith("xconv_f4_kernel"), kernel
+    assert np.array_equal(parity.unpack_words(words, layer.out_c), (~(out < 0)).astype(np.uint8)), kernel
+    assert not parity.unpack_words(words, None)[..., layer.out_c:].any(), "output bits past out_c are set"
+    parity.compare_bits(layer, inputs, words, ref=ref)
+    if not layer.use_beta and layer.iscale_dist is None:
+        pw = workloads.make_packed_input(layer, 9800 + CONV_F4.index(layer))
+        r = _packed_run(layer, inputs, pw, dev, fp4=True)
+        assert r["kernel"].startswith("xconv_f4_kernel"), r["kernel"]
+        _check_packed(layer, inputs, pw, r)
+
+
+@pytest.mark.parametrize("index", [1, 2], ids=["bench_layer", "and_layer"])
+def test_conv_fp4_measured_layer_full(dev, index):
+    """The measured XNOR + beta and AND convolutions on the fp4 matrix cores at
+    full size, every output compared with the oracle."""
+    layer = workloads.LAYERS[index]
+    inputs, ref = measured_reference(index)
+    got = parity.run_gpu(layer, inputs, dev, fp4_mfma=True)
+    assert got["main_kernel"].startswith("xconv_f4_kernel"), got["main_kernel"]
+    parity.compare(layer, inputs, got, ref=ref)
+
+
 def test_fc_fp4_unsupported_shapes(dev):
-    """BCONV_FLAG_FP4_MFMA on a convolution, or on a fully connected window
-    that is not a multiple of 4 words, is refused at creation."""
-    for layer in (workloads.BENCH_LAYER.with_(n=1), FC_TAIL[0]):
+    """BCONV_FLAG_FP4_MFMA on a convolution whose pixel is not a multiple of 4
+    words, or on a fully connected window that is not, is refused at
+    creation."""
+    for layer in (workloads.LAYERS[0], FC_TAIL[0]):
         inputs = workloads.make_inputs(layer, 9600)
         with pytest.raises(pca.BconvError) as e:
             pca.BinaryConvolution.from_layer(layer, inputs, fp4_mfma=True)
