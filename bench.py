@@ -647,7 +647,7 @@ def time_packed(pca, torch, conv, n, words, stream, warmup, steps, bits_out):
 
 # the source file that defines (and launches) each main kernel, by name prefix
 # (first matching prefix wins)
-KERNEL_FILES = {"xconv_fast": "xconv_fast.h", "xconv_generic": "xconv.hip", "xconv_small": "xconv_small.hip",
+KERNEL_FILES = {"xconv_f4": "gemm_f4.hip", "xconv_fast": "xconv_fast.h", "xconv_generic": "xconv.hip", "xconv_small": "xconv_small.hip",
                 "bgemm_f4": "gemm_f4.hip", "bgemm": "gemm.hip", "bwmma": "bwmma.hip", "bwconv": "bwconv.hip", "i8mma": "i8mma.hip",
                 "pack_vec4": "pack.hip", "pack_kernel": "pack.hip"}
 

@@ -58,6 +58,8 @@ def test_kernel_source_hash(tmp_path, monkeypatch):
     assert a == bench._kernel_sha("xconv_fast<3,3,8,1,7>")  # same source file
     assert a != bench._kernel_sha("bgemm_kernel<false>")
     assert bench._kernel_sha("bgemm_f4_kernel<false>") != bench._kernel_sha("bgemm_kernel<false>")
+    assert bench._kernel_sha("xconv_f4_kernel<true>") == bench._kernel_sha("bgemm_f4_kernel<false>")  # one file
+    assert bench._kernel_sha("xconv_f4_kernel<true>") != bench._kernel_sha("xconv_fast<3,3,8,1,7>")
     assert bench.recorded_traffic("no such workload", "xconv_fast<3,3,4,1,7>") is None
     assert bench.recorded_traffic(workloads.BENCH_LAYER.name, "bgemm_kernel<false>") is None
 
