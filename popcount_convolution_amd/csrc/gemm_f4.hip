@@ -364,13 +364,14 @@ __global__ __launch_bounds__(64 * kCF4Waves) void xconv_f4_kernel(const uint32_t
 {
     constexpr int R = kCF4R;
     __shared__ int goff[kCF4MaxGroups];  // word offset of group G from the window's first word
-    __shared__ int prect[AND ? 1 : 64 * kCF4MaxRect];  // the tile's channels' prefix tables
+    __shared__ int prect[AND ? 1 : 64 * (kCF4MaxRect + 1)];  // the tile's channels' prefix tables
     __shared__ int aoff[kCF4BetaTaps];   // A-map offset of tap t from the window's first entry
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int tile = (int)(blockIdx.x % (unsigned)tiles);
     const int m0 = (int)(blockIdx.x / (unsigned)tiles) * (16 * R * kCF4Waves) + 16 * R * wave;
     const int E = (a.kh + 1) * (a.kw + 1);
+    const int ES = E | 1;  // odd row length: lanes 16 rows apart fall in different banks
     const int taps = a.kh * a.kw;
     {
         const int wpt = a.words / 4;
@@ -382,7 +383,7 @@ __global__ __launch_bounds__(64 * kCF4Waves) void xconv_f4_kernel(const uint32_t
         if (!AND) {
             for (int i = threadIdx.x; i < 64 * E; i += 64 * kCF4Waves) {
                 const int c = i / E, co = tile * kTile + c;
-                prect[i] = co < a.out_c ? a.wrect[(long long)co * E + (i - c * E)] : 0;
+                prect[c * ES + (i - c * E)] = co < a.out_c ? a.wrect[(long long)co * E + (i - c * E)] : 0;
             }
         }
         if ((int)threadIdx.x < taps && taps <= kCF4BetaTaps) {
@@ -533,7 +534,7 @@ __global__ __launch_bounds__(64 * kCF4Waves) void xconv_f4_kernel(const uint32_t
                 const int g = 2 * pr + h;
                 const int co = tile * kTile + 16 * g + r16;
                 const bool co_ok = co < a.out_c;
-                const int *P = prect + (AND ? 0 : (16 * g + r16) * E);
+                const int *P = prect + (AND ? 0 : (16 * g + r16) * ES);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int m = m0 + 16 * f + 4 * kq + j;
