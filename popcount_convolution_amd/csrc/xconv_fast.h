@@ -136,58 +136,79 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void x
     const int oy = (int)(in_img - col * (unsigned)a.out_h);
 
     // beta of pixel `lane` (lanes < P): window sum of the zero-halo A map.
-    // Consumed in the epilogue.
-    float be_lane = 1.0f;
+    // The A values are requested here, before the first kernel row's loads,
+    // and summed only after the main loop: waiting for them here would put
+    // one more memory round trip before the first popcount of every wave.
+    constexpr int NA = (SW == 1 && NCOL <= 16) ? KH : (KH <= 4 && NCOL <= 16) ? 1 : KH * KW;
+    float av[NA];
+#pragma unroll
+    for (int i = 0; i < NA; ++i) av[i] = 0.0f;
     if (a.a_pad) {
         const __amdgpu_buffer_rsrc_t ar = make_rsrc(a.a_pad, a.apad_bytes);
         const uint32_t abase = (uint32_t)(((img * a.rows + oy * a.sh) * a.cols + ow0 * SW) * 4);
         if constexpr (SW == 1 && NCOL <= 16) {
-            // Lane c < NCOL sums column c of the strip's KH x NCOL patch; pixel
-            // `lane` then adds columns lane .. lane + KW - 1 with DPP row_shl
-            // (lane i reads lane i + kx of its 16-lane row).  Past the last
-            // column of a ragged strip the patch reads zero (buffer range) or a
-            // neighbouring pixel's value, which feed only pixels not stored.
+            // Lane c < NCOL loads column c of the strip's KH x NCOL patch.
+            // Past the last column of a ragged strip the patch reads zero
+            // (buffer range) or a neighbouring pixel's value, which feed only
+            // pixels not stored.
             const uint32_t coff = lane < NCOL ? (uint32_t)(lane * 4) : 0x80000000u;
-            float colsum = 0.0f;
 #pragma unroll
             for (int r = 0; r < KH; ++r)
-                colsum += __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ar, coff, abase + r * a.cols * 4, 0));
-            be_lane = add_row_shifted<KW>(colsum, colsum);
+                av[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ar, coff, abase + r * a.cols * 4, 0));
         } else if constexpr (KH <= 4 && NCOL <= 16) {
             // One load brings the strip's KH x NCOL patch (row r in lanes
-            // 16r..16r+15); cross-lane sums then add each window.
+            // 16r..16r+15).  The patch stays inside the zero-halo map except
+            // past the last column of a ragged strip: those read zero (buffer
+            // range) or a neighbouring pixel's value, and feed only pixels
+            // that are not stored.
             const int pr = lane >> 4, pc = lane & 15;
-            // the patch stays inside the zero-halo map except past the last
-            // column of a ragged strip: those read zero (buffer range) or a
-            // neighbouring pixel's value, and feed only pixels that are not stored
             const bool in_patch = pr < KH && pc < NCOL;
-            const float v = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                          ar, in_patch ? (uint32_t)((pr * a.cols + pc) * 4) : 0x80000000u, abase, 0));
-            float colsum = v;
-#pragma unroll
-            for (int r = 1; r < KH; ++r) colsum += __shfl(v, (lane + 16 * r) & 63);
-            float sum = 0.0f;
-#pragma unroll
-            for (int kx = 0; kx < KW; ++kx) sum += __shfl(colsum, (lane * SW + kx) & 63);
-            be_lane = sum;
+            av[0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                  ar, in_patch ? (uint32_t)((pr * a.cols + pc) * 4) : 0x80000000u, abase, 0));
         } else {
-            float sum = 0.0f;
             if (lane < P && ow0 + lane < a.out_w) {
 #pragma unroll
                 for (int ky = 0; ky < KH; ++ky)
 #pragma unroll
                     for (int kx = 0; kx < KW; ++kx)
-                        sum += __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                             ar, (uint32_t)(lane * SW * 4), abase + (ky * a.cols + kx) * 4, 0));
+                        av[ky * KW + kx] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                                          ar, (uint32_t)(lane * SW * 4), abase + (ky * a.cols + kx) * 4, 0));
             }
-            be_lane = sum;
         }
-        // window sum / (kh*kw), or / the in-image taps of the lane's pixel
-        if (a.beta_valid)
-            be_lane = be_lane / (float)window_valid_taps(oy, ow0 + lane, a.sh, SW, a.ph, a.pw, KH, KW, a.in_h, a.in_w);
-        else
-            be_lane = be_lane * (1.0f / (float)(KH * KW));
     }
+    // beta from the loaded values: the window sum / (kh*kw), or / the
+    // in-image taps of the lane's pixel.  Called after the main loop.
+    auto finish_beta = [&]() -> float {
+        if (!a.a_pad) return 1.0f;
+        // (the empty asm keeps the compiler from forming the sum, and
+        // waiting for the loads, before the main loop)
+#pragma unroll
+        for (int i = 0; i < NA; ++i) asm volatile("" : "+v"(av[i]));
+        float sum;
+        if constexpr (SW == 1 && NCOL <= 16) {
+            // lane c sums column c; pixel `lane` then adds columns lane ..
+            // lane + KW - 1 with DPP row_shl (lane i reads lane i + kx of its
+            // 16-lane row)
+            float colsum = 0.0f;
+#pragma unroll
+            for (int r = 0; r < KH; ++r) colsum += av[r];
+            sum = add_row_shifted<KW>(colsum, colsum);
+        } else if constexpr (KH <= 4 && NCOL <= 16) {
+            float colsum = av[0];
+#pragma unroll
+            for (int r = 1; r < KH; ++r) colsum += __shfl(av[0], (lane + 16 * r) & 63);
+            sum = 0.0f;
+#pragma unroll
+            for (int kx = 0; kx < KW; ++kx) sum += __shfl(colsum, (lane * SW + kx) & 63);
+        } else {
+            sum = 0.0f;
+#pragma unroll
+            for (int i = 0; i < NA; ++i) sum += av[i];
+        }
+        if (a.beta_valid)
+            return sum / (float)window_valid_taps(oy, ow0 + lane, a.sh, SW, a.ph, a.pw, KH, KW, a.in_h, a.in_w);
+        return sum * (1.0f / (float)(KH * KW));
+    };
 
     // Epilogue operands are loaded here, so their latency overlaps the first
     // kernel row's loads instead of sitting at the end of the wave.
@@ -288,6 +309,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void x
         }
     }
 
+    const float be_lane = finish_beta();
     if (a.a_pad && tile == 0 && lane < P && ow0 + lane < a.out_w)
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, be_lane), make_rsrc(a.beta_out, a.beta_bytes),
                                               (uint32_t)(lane * 4), (uint32_t)(((img * a.out_h + oy) * a.out_w + ow0) * 4), 0);
