@@ -30,6 +30,8 @@ struct PackArgs {
     long long halo_a;       // n*halo_pixels_per_image (A map halo entries)
     int n;
     FastDiv div_in_h;       // by in_h (image and row of a packed row index)
+    int bits_bytes, a_bytes;  // padded bit buffer and A map sizes (vector path: < 2^31)
+    float inv_c;            // 1 / in_c, rounded once on the host
 };
 
 __device__ __forceinline__ void halo_pixel(const PackArgs &a, unsigned i, int &row, int &col)
@@ -121,18 +123,44 @@ __device__ __forceinline__ uint32_t group_or(uint32_t v)
     if (N >= 8) v |= dpp_u32<kDppHalfMirror>(v);
     return v;
 }
-// Sum over aligned groups of N lanes (N <= 64), in a fixed order.
+// Sum over aligned groups of N lanes (N <= 64), in a fixed order, without
+// LDS: a butterfly within each 16-lane row (every lane ends with the same
+// row sum), then the row sums are combined with the row broadcasts of DPP (lane 15 of a row added into the next row, lane 31
+// into the last row), so only the group's last row holds the whole sum.
+// Lane `group_sum_lane<N>()` of each group (and the lanes after it) has it.
 template <int N>
-__device__ __forceinline__ float group_sum(float v)
+__device__ __forceinline__ float group_sum_last(float v)
 {
+    constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
     if (N >= 2) v += dpp_f32<kDppXor1>(v);
     if (N >= 4) v += dpp_f32<kDppXor2>(v);
     if (N >= 8) v += dpp_f32<kDppHalfMirror>(v);
     if (N >= 16) v += dpp_f32<kDppMirror>(v);
-    if (N >= 32) v += __shfl_xor(v, 16, 64);
-    if (N >= 64) v += __shfl_xor(v, 32, 64);
+    if (N >= 32)  // rows 1 and 3 += lane 15 of rows 0 and 2
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppRowBcast15, 0xA, 0xF, false));
+    if (N >= 64)  // row 3 += lane 31 (rows 0 + 1)
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppRowBcast31, 0x8, 0xF, false));
     return v;
 }
+template <int N>
+constexpr int group_sum_lane() { return N >= 64 ? 48 : N >= 32 ? 16 : 0; }
+
+// The value, held in SGPRs and opaque to the compiler from here on (so it is
+// neither re-read from the argument segment nor moved before this point).
+__device__ __forceinline__ uint32_t pin_sgpr(uint32_t v)
+{
+    asm volatile("" : "+s"(v));
+    return v;
+}
+template <typename T>
+__device__ __forceinline__ T *pin_sgpr(T *p)
+{
+    uint64_t v = reinterpret_cast<uint64_t>(p);
+    asm volatile("" : "+s"(v));
+    return reinterpret_cast<T *>(v);
+}
+
+constexpr uint32_t kOob = 0x80000000u;  // buffer offset past any range: loads read 0, stores are dropped
 
 // Fast path: in_c % 4 == 0 and a 16-byte aligned input.  A pixel's channels
 // are spread over SEG lanes, four consecutive channels (one float4) per lane
@@ -146,17 +174,32 @@ __device__ __forceinline__ float group_sum(float v)
 // stores go through buffer descriptors: a scalar base plus a lane offset.
 // The arguments the first loads need come first, as scalars, so the hardware
 // preloads them into SGPRs before the wave starts (no kernel-argument round
-// trip before the input is requested); the rest are in `a`, fetched while
-// the input loads are in flight.  A 32-channel word is the OR of 8 lanes'
-// 4-bit groups (DPP), |x'| is summed per lane and then over the pixel's
-// lanes in a fixed order.
+// trip before the input is requested); the rest are in the argument struct,
+// read through the kernel-argument segment pointer where they are needed, so
+// their fetch overlaps the input loads (taken as an ordinary parameter, the
+// compiler loads the whole struct at kernel entry, and reusing one of its
+// registers before that load returns makes the input loads wait for it).
+// A 32-channel word is the OR of 8 lanes' 4-bit groups (DPP), |x'| is summed
+// per lane and then over the pixel's lanes in a fixed order.
+//
+// Byte offset of the struct in the argument segment: explicit arguments are
+// laid out in order, each at its natural alignment (a pointer, nine 32-bit
+// scalars, then the struct).
+constexpr unsigned kPackArgsOffset =
+    (unsigned)((sizeof(const float *) + 9 * sizeof(int) + alignof(PackArgs) - 1) / alignof(PackArgs) * alignof(PackArgs));
+static_assert(kPackArgsOffset == 48, "argument layout of pack_vec4");
+
 template <int SEG, int U, int NC>
 __global__ __launch_bounds__(256) void pack_vec4(const float *x, int x_bytes, int in_c, int in_w, int row_count,
                                                  int runs_per_row, uint32_t rpr_m, int rpr_s, uint32_t rpr_id,
-                                                 int pack_blocks, PackArgs a)
+                                                 int pack_blocks, PackArgs /* read via the segment pointer */)
 {
+    // (constant address space: stores cannot alias it, so fields are not re-read)
+    typedef const __attribute__((address_space(4))) PackArgs *ArgsPtr;
+    typedef const __attribute__((address_space(4))) char *ArgBytes;
+    const ArgsPtr ap = (ArgsPtr)((ArgBytes)__builtin_amdgcn_kernarg_segment_ptr() + kPackArgsOffset);
     if ((int)blockIdx.x >= pack_blocks) {
-        clear_halo(a, (long long)(blockIdx.x - pack_blocks) * blockDim.x + threadIdx.x);
+        clear_halo(*(const PackArgs *)ap, (long long)(blockIdx.x - pack_blocks) * 256 + threadIdx.x);
         return;
     }
     constexpr int G = 64 / SEG;
@@ -167,44 +210,64 @@ __global__ __launch_bounds__(256) void pack_vec4(const float *x, int x_bytes, in
     const int slot = lane / SEG;
     const int sl = lane % SEG;
     // wave -> (image row, run of RUN pixels in it); all uniform
-    const unsigned wave = blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // (4 waves per workgroup: the launch shape, fixed, so no kernel-argument
+    // load is needed before the first input loads)
+    const unsigned wave = blockIdx.x * 4u + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const unsigned row_id = fastdiv(wave, FastDiv{rpr_m, rpr_s, rpr_id});  // img * in_h + y
     if (row_id >= (unsigned)row_count) return;
     const int x0 = (int)(wave - row_id * (unsigned)runs_per_row) * RUN;
     const uint32_t in_base = (row_id * (unsigned)in_w + (unsigned)x0) * (unsigned)in_c * 4u;
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, x_bytes);
-    // the input affine's arrays come with the argument struct; their loads
-    // are only needed once the input has arrived
-    const float *in_scale = a.in_scale, *in_bias = a.in_bias;
-    const bool affine = in_scale != nullptr || in_bias != nullptr;
-    float asum[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) asum[u] = 0.0f;
-    for (int c00 = 0; c00 < in_c; c00 += NCH * SEG * 4) {
-        float4 v[NCH][U], s4[NCH], b4[NCH];
+    // A lane's 16-byte input loads of one chunk of NCH*SEG*4 channels;
+    // inactive lanes read 0 through the range check.
+    float4 v[NCH][U];
+    auto load_chunk = [&](int c00) {
 #pragma unroll
         for (int k = 0; k < NCH; ++k) {
             const int c = c00 + k * SEG * 4 + sl * 4;
             const bool cact = c < in_c;
-            s4[k] = make_float4(1.f, 1.f, 1.f, 1.f);
-            b4[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (cact && in_scale) s4[k] = *reinterpret_cast<const float4 *>(in_scale + c);
-            if (cact && in_bias) b4[k] = *reinterpret_cast<const float4 *>(in_bias + c);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int px = x0 + u * G + slot;
-                v[k][u] = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (cact && px < in_w)
-                    v[k][u] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                             xr, (uint32_t)((u * G + slot) * in_c + c) * 4u, in_base, 0));
+                const uint32_t off = cact && px < in_w ? (uint32_t)((u * G + slot) * in_c + c) * 4u : kOob;
+                v[k][u] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, in_base, 0));
             }
         }
-        // the store side's geometry, from the argument struct (its loads
-        // overlap the input loads above)
-        const unsigned img = fastdiv(row_id, a.div_in_h);
-        const unsigned y = row_id - img * (unsigned)a.in_h;
-        const uint32_t pad_base = ((img * (unsigned)a.rows + y + (unsigned)a.halo_h) * (unsigned)a.cols +
-                                   (unsigned)(x0 + a.halo_w));  // padded pixel index of x0
+    };
+    load_chunk(0);
+    // Only now the argument struct: its fields are read once and pinned in
+    // SGPRs (left to itself the compiler re-reads them before every store).
+    const float *in_scale = pin_sgpr(ap->in_scale), *in_bias = pin_sgpr(ap->in_bias);
+    const bool affine = in_scale != nullptr || in_bias != nullptr;
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(in_scale, in_c * 4), bir = make_rsrc(in_bias, in_c * 4);
+    uint32_t *const bits = pin_sgpr(ap->bits);
+    float *const a_map = pin_sgpr(ap->a_map);
+    const uint32_t words = pin_sgpr((uint32_t)ap->words);
+    const __amdgpu_buffer_rsrc_t br = make_rsrc(bits, (int)pin_sgpr((uint32_t)ap->bits_bytes));
+    const __amdgpu_buffer_rsrc_t amr = make_rsrc(a_map, (int)pin_sgpr((uint32_t)ap->a_bytes));
+    const float inv_c = __uint_as_float(pin_sgpr(__float_as_uint(ap->inv_c)));
+    // padded pixel index of x0
+    const FastDiv div_in_h{ap->div_in_h.m, ap->div_in_h.s, ap->div_in_h.id};
+    const unsigned img = fastdiv(row_id, div_in_h);
+    const unsigned y = row_id - img * (unsigned)ap->in_h;
+    const uint32_t pad_base = pin_sgpr((img * (unsigned)ap->rows + y + (unsigned)ap->halo_h) * (unsigned)ap->cols +
+                                       (unsigned)(x0 + ap->halo_w));
+    float asum[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) asum[u] = 0.0f;
+    for (int c00 = 0;;) {
+        float4 s4[NCH], b4[NCH];
+#pragma unroll
+        for (int k = 0; k < NCH; ++k) {
+            const int c = c00 + k * SEG * 4 + sl * 4;
+            const bool cact = c < in_c;
+            // channels past in_c read 0 (their input is 0 too, so t = 0)
+            const uint32_t off = cact ? (uint32_t)c * 4u : kOob;
+            s4[k] = make_float4(1.f, 1.f, 1.f, 1.f);
+            b4[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (in_scale) s4[k] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(sr, off, 0, 0));
+            if (in_bias) b4[k] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(bir, off, 0, 0));
+        }
 #pragma unroll
         for (int k = 0; k < NCH; ++k) {
             const int c = c00 + k * SEG * 4 + sl * 4;
@@ -226,25 +289,27 @@ __global__ __launch_bounds__(256) void pack_vec4(const float *x, int x_bytes, in
                     asum[u] += fabsf(t[j]);
                 }
                 if (!cact) nib = 0;  // channels past in_c are zero bits, not signs of 0
-                if (a.bits) {
+                if (bits) {
+                    // one lane per word stores (agent-scope write-through);
+                    // the others aim past the buffer and are dropped
                     const uint32_t word = group_or<LPW>(nib << ((sl * 4) & 31));
-                    if (cact && px < in_w && (sl % LPW) == 0)
-                        store_through(&a.bits[((long long)pad_base + u * G + slot) * a.words + c / 32], word);
+                    const bool st = cact && px < in_w && (sl % LPW) == 0;
+                    const uint32_t off = st ? ((pad_base + (uint32_t)(u * G + slot)) * words + (uint32_t)(c / 32)) * 4u : kOob;
+                    __builtin_amdgcn_raw_buffer_store_b32(word, br, off, 0, kStoreSc1);
                 }
             }
         }
-        if (NC > 0) break;  // all chunks done
+        c00 += NCH * SEG * 4;
+        if (NC > 0 || c00 >= in_c) break;  // all chunks done
+        load_chunk(c00);
     }
-    if (a.a_map) {
-        const unsigned img = fastdiv(row_id, a.div_in_h);
-        const unsigned y = row_id - img * (unsigned)a.in_h;
-        const uint32_t pad_base = ((img * (unsigned)a.rows + y + (unsigned)a.halo_h) * (unsigned)a.cols +
-                                   (unsigned)(x0 + a.halo_w));
-        const float inv_c = 1.0f / (float)in_c;
+    if (a_map) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const float s = group_sum<SEG>(asum[u]);
-            if (sl == 0 && x0 + u * G + slot < in_w) store_through(&a.a_map[(long long)pad_base + u * G + slot], s * inv_c);
+            const float s = group_sum_last<SEG>(asum[u]);
+            const bool st = sl == group_sum_lane<SEG>() && x0 + u * G + slot < in_w;
+            const uint32_t off = st ? (pad_base + (uint32_t)(u * G + slot)) * 4u : kOob;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s * inv_c), amr, off, 0, kStoreSc1);
         }
     }
 }
@@ -376,8 +441,14 @@ hipError_t launch_pack(const Geom &g, const Launch &s, const float *x, const flo
     const long long halo_blocks = (a.halo_words + a.slack_words + a.halo_a + 255) / 256;
     if (a.pixels == 0) return hipSuccess;
 
+    const long long bits_bytes = bits ? ((long long)g.n * g.bits_rows * g.bits_cols * g.words + g.bits_slack_words) * 4 : 0;
+    const long long a_bytes = a_map ? (long long)g.n * g.bits_rows * g.bits_cols * 4 : 0;
+    a.bits_bytes = (int)(bits_bytes < 0x7fffffffLL ? bits_bytes : 0);
+    a.a_bytes = (int)(a_bytes < 0x7fffffffLL ? a_bytes : 0);
+    a.inv_c = 1.0f / (float)g.in_c;
     const bool vec4 = g.in_c % 4 == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0 &&
                       (long long)g.n * g.in_h * g.in_w * g.in_c * 4 < 0x7fffffffLL &&
+                      bits_bytes < 0x7fffffffLL && a_bytes < 0x7fffffffLL &&
                       (reinterpret_cast<uintptr_t>(in_scale) & 15) == 0 &&
                       (reinterpret_cast<uintptr_t>(in_bias) & 15) == 0;
     const int vec = vec4 ? 4 : 1;
