@@ -110,6 +110,7 @@ def _sweep_layers():
         dict(n=1, in_h=16, in_w=16, in_c=96, out_c=64),
         dict(n=1, in_h=8, in_w=56, in_c=128, out_c=128),
         dict(n=1, in_h=7, in_w=28, in_c=256, out_c=256),
+        dict(n=2, in_h=5, in_w=6, in_c=1000, out_c=40),                # pack: channel chunks in a loop
     ]
     out = []
     for gi, gd in enumerate(geoms):
