@@ -303,7 +303,24 @@ __global__ __launch_bounds__(256) void pack_vec4(const float *x, int x_bytes, in
         if (NC > 0 || c00 >= in_c) break;  // all chunks done
         load_chunk(c00);
     }
-    if (a_map) {
+    if constexpr (RUN <= 64) {
+        // The wave's RUN pixels have contiguous A entries: one store of RUN
+        // lanes after a lane permute (pixel p's sum sits in lane
+        // (p%G)*SEG + group_sum_lane of pass p/G), instead of one partial
+        // store per pass.
+        if (a_map) {
+            const int src = ((lane % G) * SEG + group_sum_lane<SEG>()) * 4;
+            float s = 0.0f;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const float t = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(group_sum_last<SEG>(asum[u]))));
+                if (lane / G == u) s = t;
+            }
+            const bool st = lane < RUN && x0 + lane < in_w;
+            const uint32_t off = st ? (pad_base + (uint32_t)lane) * 4u : kOob;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s * inv_c), amr, off, 0, kStoreSc1);
+        }
+    } else if (a_map) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const float s = group_sum_last<SEG>(asum[u]);
