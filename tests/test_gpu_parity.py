@@ -111,6 +111,9 @@ def _sweep_layers():
         dict(n=1, in_h=8, in_w=56, in_c=128, out_c=128),
         dict(n=1, in_h=7, in_w=28, in_c=256, out_c=256),
         dict(n=2, in_h=5, in_w=6, in_c=1000, out_c=40),                # pack: channel chunks in a loop
+        dict(n=2, in_h=7, in_w=37, in_c=12, out_c=24),                 # pack: 16 pixels a pass, ragged runs
+        dict(n=2, in_h=5, in_w=70, in_c=8, out_c=16),                  # pack: 32 pixels a pass
+        dict(n=1, in_h=6, in_w=9, in_c=20, out_c=9),                   # pack: 8 lanes a pixel, idle lanes
     ]
     out = []
     for gi, gd in enumerate(geoms):
