@@ -114,6 +114,7 @@ def _sweep_layers():
         dict(n=2, in_h=7, in_w=37, in_c=12, out_c=24),                 # pack: 16 pixels a pass, ragged runs
         dict(n=2, in_h=5, in_w=70, in_c=8, out_c=16),                  # pack: 32 pixels a pass
         dict(n=1, in_h=6, in_w=9, in_c=20, out_c=9),                   # pack: 8 lanes a pixel, idle lanes
+        dict(n=3, in_h=3, in_w=5, in_c=768, out_c=24, kernel_h=3, kernel_w=3, pad_h=0, pad_w=0),  # 256-channel parts
     ]
     out = []
     for gi, gd in enumerate(geoms):
